@@ -1,0 +1,332 @@
+// C ABI of the library: argument checking on the host, then launches.
+// Nothing here allocates or synchronizes; see include/bql.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "bql.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bql_status fail(bql_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bql_status ok() {
+    g_err[0] = '\0';
+    return BQL_OK;
+}
+
+#define CHECK(expr)                              \
+    do {                                         \
+        bql_status st__ = (expr);                \
+        if (st__ != BQL_OK) return st__;         \
+    } while (0)
+
+bql_status need_ptr(const void* p, const char* name) {
+    if (!p) return fail(BQL_ERR_NULL, "%s is NULL", name);
+    if (((uintptr_t)p) & 15u) return fail(BQL_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return BQL_OK;
+}
+
+// Scalars (one fp32) only need natural alignment.
+bql_status need_scalar(const void* p, const char* name) {
+    if (!p) return fail(BQL_ERR_NULL, "%s is NULL", name);
+    if (((uintptr_t)p) & 3u) return fail(BQL_ERR_ALIGN, "%s is not 4-byte aligned", name);
+    return BQL_OK;
+}
+
+constexpr int64_t MAX_DIM = int64_t(1) << 24;
+
+bql_status need_nk(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return fail(BQL_ERR_SHAPE, "N=%lld and K=%lld must be positive", (long long)N, (long long)K);
+    if (N % 16 || K % 16)
+        return fail(BQL_ERR_SHAPE, "N=%lld and K=%lld must be multiples of 16", (long long)N, (long long)K);
+    if (N > MAX_DIM || K > MAX_DIM) return fail(BQL_ERR_SHAPE, "N or K above 2^24");
+    return BQL_OK;
+}
+
+bql_status need_m(int64_t M) {
+    if (M < 0) return fail(BQL_ERR_SHAPE, "M=%lld is negative", (long long)M);
+    if (M > (int64_t(1) << 22)) return fail(BQL_ERR_SHAPE, "M above 2^22");
+    return BQL_OK;
+}
+
+bql_status need_ws(void* ws, size_t have, size_t want) {
+    if (want == 0) return BQL_OK;
+    if (!ws) return fail(BQL_ERR_WORKSPACE, "workspace of %zu bytes is required", want);
+    if (((uintptr_t)ws) & 255u) return fail(BQL_ERR_ALIGN, "workspace is not 256-byte aligned");
+    if (have < want) return fail(BQL_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, want);
+    return BQL_OK;
+}
+
+bool is_f16ish(bql_dtype d) { return d == BQL_F16 || d == BQL_BF16; }
+
+bql_status hip_status(hipError_t e) {
+    if (e != hipSuccess) return fail(BQL_ERR_HIP, "HIP: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t ktiles(int64_t K) { return (K + 127) / 128; }
+
+}  // namespace
+
+extern "C" {
+
+int bql_abi_version(void) { return BQL_ABI_VERSION; }
+
+const char* bql_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------- quantizers
+
+size_t bql_quantize_workspace_size(int64_t numel) {
+    (void)numel;
+    return bql::QUANT_WS_BYTES;
+}
+
+bql_status bql_fp8_quantize_dynamic(const void* x, bql_dtype xdt, int64_t numel, uint8_t* xq,
+                                    float* scale_out, void* ws, size_t ws_bytes,
+                                    bql_stream stream) {
+    if (numel < 0) return fail(BQL_ERR_SHAPE, "numel is negative");
+    if (!is_f16ish(xdt)) return fail(BQL_ERR_DTYPE, "x must be BQL_F16 or BQL_BF16");
+    CHECK(need_ptr(x, "x"));
+    CHECK(need_ptr(xq, "xq"));
+    if (scale_out && (((uintptr_t)scale_out) & 3u)) return fail(BQL_ERR_ALIGN, "scale_out misaligned");
+    CHECK(need_ws(ws, ws_bytes, bql_quantize_workspace_size(numel)));
+    if (numel == 0) return ok();
+    return hip_status(bql::launch_quant_dynamic(x, xdt, numel, xq, scale_out, ws, (hipStream_t)stream));
+}
+
+bql_status bql_fp8_quantize_static(const void* x, bql_dtype xdt, int64_t numel, const float* scale,
+                                   uint8_t* xq, bql_stream stream) {
+    if (numel < 0) return fail(BQL_ERR_SHAPE, "numel is negative");
+    if (!is_f16ish(xdt)) return fail(BQL_ERR_DTYPE, "x must be BQL_F16 or BQL_BF16");
+    CHECK(need_ptr(x, "x"));
+    CHECK(need_ptr(xq, "xq"));
+    CHECK(need_scalar(scale, "scale"));
+    if (numel == 0) return ok();
+    return hip_status(bql::launch_quant_static(x, xdt, numel, scale, xq, (hipStream_t)stream));
+}
+
+bql_status bql_int8_quantize_per_token(const void* x, bql_dtype xdt, int64_t M, int64_t K,
+                                       int8_t* xq, float* scales, bql_stream stream) {
+    if (!is_f16ish(xdt)) return fail(BQL_ERR_DTYPE, "x must be BQL_F16 or BQL_BF16");
+    CHECK(need_m(M));
+    if (K <= 0 || K % 16 || K > MAX_DIM) return fail(BQL_ERR_SHAPE, "K must be a positive multiple of 16");
+    if (M > 0x7FFFFFFF) return fail(BQL_ERR_SHAPE, "M too large");
+    CHECK(need_ptr(x, "x"));
+    CHECK(need_ptr(xq, "xq"));
+    CHECK(need_ptr(scales, "scales"));
+    if (M == 0) return ok();
+    return hip_status(bql::launch_int8_per_token(x, xdt, M, K, xq, scales, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- prepack
+
+size_t bql_packed_weight_bytes(int64_t N, int64_t K, bql_wfmt fmt) {
+    if (N <= 0 || K <= 0) return 0;
+    const size_t tiles = (size_t)((N + 15) / 16) * (size_t)ktiles(K);
+    return tiles * (fmt == BQL_WFMT_INT4_CHANNEL ? 1024 : 2048);
+}
+
+size_t bql_prepack_workspace_size(int64_t N, int64_t K, bql_wfmt fmt) {
+    (void)N; (void)K;
+    return fmt == BQL_WFMT_FP8_TENSOR ? bql::QUANT_WS_BYTES : 0;
+}
+
+bql_status bql_prepack_weight(const void* w, bql_dtype wdt, int64_t N, int64_t K, bql_wfmt fmt,
+                              const void* scales_in, bql_dtype sdt, void* packed,
+                              float* scales_out, void* ws, size_t ws_bytes, bql_stream stream) {
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(need_nk(N, K));
+    CHECK(need_ptr(w, "w"));
+    CHECK(need_ptr(packed, "packed"));
+    CHECK(need_ptr(scales_out, "scales_out"));
+    if (fmt != BQL_WFMT_FP8_TENSOR && fmt != BQL_WFMT_FP8_CHANNEL && fmt != BQL_WFMT_INT4_CHANNEL)
+        return fail(BQL_ERR_ARG, "unknown weight format %d", (int)fmt);
+    const int64_t nscales = fmt == BQL_WFMT_FP8_TENSOR ? 1 : N;
+    if (scales_in) {
+        if (sdt != BQL_F16 && sdt != BQL_F32) return fail(BQL_ERR_DTYPE, "scales must be BQL_F16 or BQL_F32");
+        CHECK(need_scalar(scales_in, "scales_in"));
+        if (sdt == BQL_F16 && (((uintptr_t)scales_in) & 1u)) return fail(BQL_ERR_ALIGN, "scales_in misaligned");
+    }
+    if (fmt == BQL_WFMT_INT4_CHANNEL) {
+        if (wdt != BQL_INT4) return fail(BQL_ERR_DTYPE, "INT4_CHANNEL takes a BQL_INT4 weight");
+        if (!scales_in) return fail(BQL_ERR_NULL, "INT4_CHANNEL needs scales_in");
+        hipError_t e = bql::launch_convert_scales(scales_in, sdt == BQL_F16 ? 1 : 3, nscales, scales_out, s);
+        if (e == hipSuccess) e = bql::launch_prepack_int4((const uint8_t*)w, N, K, (uint8_t*)packed, s);
+        return hip_status(e);
+    }
+    if (wdt != BQL_F16 && wdt != BQL_BF16 && wdt != BQL_E4M3)
+        return fail(BQL_ERR_DTYPE, "FP8 formats take a BQL_F16, BQL_BF16 or BQL_E4M3 weight");
+    hipError_t e = hipSuccess;
+    if (scales_in) {
+        e = bql::launch_convert_scales(scales_in, sdt == BQL_F16 ? 1 : 3, nscales, scales_out, s);
+    } else {
+        if (wdt == BQL_E4M3) return fail(BQL_ERR_NULL, "an E4M3 weight needs scales_in");
+        if (fmt == BQL_WFMT_FP8_TENSOR) {
+            CHECK(need_ws(ws, ws_bytes, bql_prepack_workspace_size(N, K, fmt)));
+            e = bql::launch_tensor_scale(w, wdt, N * K, 448.0f, scales_out, ws, s);
+        } else {
+            e = bql::launch_row_scales(w, wdt, N, K, 448.0f, scales_out, s);
+        }
+    }
+    if (e == hipSuccess)
+        e = bql::launch_prepack_fp8(w, (int)wdt, N, K, scales_out, fmt == BQL_WFMT_FP8_CHANNEL,
+                                    (uint8_t*)packed, s);
+    return hip_status(e);
+}
+
+bql_status bql_unpack_weight(const void* packed, int64_t N, int64_t K, bql_wfmt fmt, void* out,
+                             bql_stream stream) {
+    CHECK(need_nk(N, K));
+    CHECK(need_ptr(packed, "packed"));
+    CHECK(need_ptr(out, "out"));
+    if (fmt == BQL_WFMT_INT4_CHANNEL)
+        return hip_status(bql::launch_unpack_int4((const uint8_t*)packed, N, K, (uint8_t*)out, (hipStream_t)stream));
+    if (fmt == BQL_WFMT_FP8_TENSOR || fmt == BQL_WFMT_FP8_CHANNEL)
+        return hip_status(bql::launch_unpack_fp8((const uint8_t*)packed, N, K, (uint8_t*)out, (hipStream_t)stream));
+    return fail(BQL_ERR_ARG, "unknown weight format %d", (int)fmt);
+}
+
+// ---------------------------------------------------------------- linears
+
+// fp8 workspace: [quantizer partials + scale: 8 KiB][Aq: M*K][split-K partials]
+size_t bql_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return bql::QUANT_WS_BYTES + align256((size_t)M * K) + align256(bql::small_m_ws_bytes(M, N, K, bql::V_FP8));
+}
+
+bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const void* w_packed,
+                          const float* w_scale, int w_per_channel, int64_t M, int64_t N, int64_t K,
+                          const float* output_scale, void* y, bql_dtype ydt, bql_accum accum,
+                          void* ws, size_t ws_bytes, bql_stream stream) {
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(need_m(M));
+    CHECK(need_nk(N, K));
+    if (!is_f16ish(adt) && adt != BQL_E4M3) return fail(BQL_ERR_DTYPE, "A must be BQL_F16, BQL_BF16 or BQL_E4M3");
+    if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_E4M3)
+        return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16, BQL_F32 or BQL_E4M3");
+    if (w_per_channel != 0 && w_per_channel != 1) return fail(BQL_ERR_ARG, "w_per_channel must be 0 or 1");
+    if (accum != BQL_ACCUM_EXACT && accum != BQL_ACCUM_FAST) return fail(BQL_ERR_ARG, "unknown accum %d", (int)accum);
+    if (M == 0) return ok();
+    CHECK(need_ptr(a, "a"));
+    CHECK(need_ptr(w_packed, "w_packed"));
+    CHECK(need_scalar(w_scale, "w_scale"));
+    CHECK(need_ptr(y, "y"));
+    if (adt == BQL_E4M3) CHECK(need_scalar(a_scale, "a_scale"));
+    else if (a_scale && (((uintptr_t)a_scale) & 3u)) return fail(BQL_ERR_ALIGN, "a_scale misaligned");
+    if (ydt == BQL_E4M3) CHECK(need_scalar(output_scale, "output_scale"));
+    CHECK(need_ws(ws, ws_bytes, bql_fp8_linear_workspace_size(M, N, K)));
+
+    char* wsb = (char*)ws;
+    const uint8_t* aq = (const uint8_t*)a;
+    const float* sa = a_scale;
+    if (adt != BQL_E4M3) {
+        uint8_t* aq_ws = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);
+        hipError_t e = bql::launch_quant_dynamic(a, adt, M * K, aq_ws, a_scale, wsb, s);
+        if (e != hipSuccess) return hip_status(e);
+        aq = aq_ws;
+        sa = (const float*)(wsb + 4096);
+    }
+    bql::LinearArgs la;
+    la.variant = accum == BQL_ACCUM_FAST ? bql::V_FP8 : bql::V_FP8X;
+    la.a = aq;
+    la.w = (const uint8_t*)w_packed;
+    la.M = M;
+    la.N = N;
+    la.K = K;
+    la.y = y;
+    la.ydt = ydt;
+    la.a_scale = sa;
+    la.w_scale = w_scale;
+    la.w_per_channel = w_per_channel;
+    la.out_scale = output_scale;
+    char* part = wsb + bql::QUANT_WS_BYTES + align256((size_t)M * K);
+    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_FP8), s));
+}
+
+size_t bql_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return align256(bql::small_m_ws_bytes(M, N, K, bql::V_W8A16));
+}
+
+bql_status bql_w8a16_linear(const void* a, const void* w_packed, const float* w_scales, int64_t M,
+                            int64_t N, int64_t K, void* y, bql_dtype ydt, void* ws, size_t ws_bytes,
+                            bql_stream stream) {
+    CHECK(need_m(M));
+    CHECK(need_nk(N, K));
+    if (M > (int64_t(65535) * 16)) return fail(BQL_ERR_SHAPE, "M above 1048560");
+    if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32)
+        return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16 or BQL_F32");
+    if (M == 0) return ok();
+    CHECK(need_ptr(a, "a"));
+    CHECK(need_ptr(w_packed, "w_packed"));
+    CHECK(need_ptr(w_scales, "w_scales"));
+    CHECK(need_ptr(y, "y"));
+    CHECK(need_ws(ws, ws_bytes, bql_w8a16_linear_workspace_size(M, N, K)));
+    bql::LinearArgs la;
+    la.variant = bql::V_W8A16;
+    la.a = a;
+    la.w = (const uint8_t*)w_packed;
+    la.M = M;
+    la.N = N;
+    la.K = K;
+    la.y = y;
+    la.ydt = ydt;
+    la.a_scale = nullptr;
+    la.w_scale = w_scales;
+    la.w_per_channel = 1;
+    la.out_scale = nullptr;
+    return hip_status(bql::launch_linear(la, ws, ws_bytes, (hipStream_t)stream));
+}
+
+size_t bql_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return align256(bql::small_m_ws_bytes(M, N, K, bql::V_W4A8));
+}
+
+bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* w_packed,
+                           const float* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                           bql_dtype ydt, void* ws, size_t ws_bytes, bql_stream stream) {
+    CHECK(need_m(M));
+    CHECK(need_nk(N, K));
+    if (K > 131072) return fail(BQL_ERR_SHAPE, "K above 131072 could overflow the int32 accumulator");
+    if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_I32)
+        return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16, BQL_F32 or BQL_I32");
+    if (M == 0) return ok();
+    CHECK(need_ptr(aq, "aq"));
+    CHECK(need_ptr(w_packed, "w_packed"));
+    CHECK(need_ptr(y, "y"));
+    if (ydt != BQL_I32) {
+        CHECK(need_ptr(a_scales, "a_scales"));
+        CHECK(need_ptr(w_scales, "w_scales"));
+    }
+    CHECK(need_ws(ws, ws_bytes, bql_w4a8_linear_workspace_size(M, N, K)));
+    bql::LinearArgs la;
+    la.variant = bql::V_W4A8;
+    la.a = aq;
+    la.w = (const uint8_t*)w_packed;
+    la.M = M;
+    la.N = N;
+    la.K = K;
+    la.y = y;
+    la.ydt = ydt;
+    la.a_scale = a_scales;
+    la.w_scale = w_scales;
+    la.w_per_channel = 1;
+    la.out_scale = nullptr;
+    return hip_status(bql::launch_linear(la, ws, ws_bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+// Device-side helpers shared by the gfx950 kernels of the library.
+//
+// E4M3 here is the OCP FP8 E4M3 format named by the vLLM FP8
+// quantization-schema RFC (Scope): bias 7, three mantissa bits, no
+// infinity, S.1111.111 = NaN, largest finite 448.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bql {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+enum InDtype { IN_F16 = 1, IN_BF16 = 2 };
+enum OutDtype { OUT_F16 = 1, OUT_BF16 = 2, OUT_F32 = 3, OUT_E4M3 = 4, OUT_I32 = 6 };
+
+// Packed-weight tiles: 16 output channels x 128 k.  FP8 tiles hold 2048
+// bytes as [half h][lane l][16 bytes]; lane l covers channel l % 16 and
+// k = 32*(l/16) + 16*h + j.  INT4 tiles hold 1024 bytes as [lane][16 bytes];
+// byte j of lane l has k = 32*(l/16) + j in its low nibble and k + 16 in its
+// high nibble.  Tiles of one 16-channel strip are consecutive along k.
+constexpr int TILE_N = 16;
+constexpr int TILE_K = 128;
+constexpr int FP8_TILE_BYTES = 2048;
+constexpr int INT4_TILE_BYTES = 1024;
+
+// ----------------------------------------------------------- conversions
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint32_t bits16) {
+    if constexpr (DT == IN_BF16) {
+        return __uint_as_float(bits16 << 16);
+    } else {
+        _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+        return (float)h;
+    }
+}
+
+// |x| as an integer that orders like |x| (non-NaN), for an exact amax.
+__device__ __forceinline__ uint32_t mag16(uint32_t bits16) { return bits16 & 0x7FFFu; }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // nearest, ties to even
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32: nearest, ties to even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// fp32 -> OCP E4M3 code: round to nearest even on the bit pattern,
+// saturate magnitudes >= 448 to 0x7E, keep the sign (so -0 -> 0x80).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t s = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return s | 0x7Fu;  // NaN
+    if (a >= 0x43E00000u) return s | 0x7Eu; // |v| >= 448
+    if (a < 0x3C800000u) {                  // |v| < 2^-6: subnormal grid of 2^-9
+        float t = __uint_as_float(a) * 512.0f;  // exact scaling
+        return s | (uint32_t)__builtin_rintf(t);
+    }
+    // normal: keep 3 of 23 mantissa bits with ties to even, carry into the
+    // exponent, then rebias the exponent from 127 to 7 (120 << 3 = 960)
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return s | ((r >> 20) - 960u);
+}
+
+// ------------------------------------------------------------- reductions
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = __shfl_xor(v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Max over the block, returned to every thread.  `sh` holds >= 16 words.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    uint32_t m = 0;
+    for (int i = 0; i < nw; ++i) m = m > sh[i] ? m : sh[i];
+    return m;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
+    // scale operands of 0 select the unscaled v_mfma_f32_16x16x128_f8f6f4;
+    // format 0 for both operands is E4M3
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4i mfma_i8(const v4i& a, const v4i& b, const v4i& c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (two dwords, bytes in k order) -> eight fp16 with the
+// same values.  Every finite E4M3 value (|v| <= 448, subnormals down to
+// 2^-9) is an fp16 value, so v_cvt_scalef32_pk_f16_fp8 with scale 1.0 is
+// lossless; fp16 x fp16 products are exact in the fp32 matrix-core sum.
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t d0, uint32_t d1) {
+    v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)d0, 1.0f, false);
+    v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)d0, 1.0f, true);
+    v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)d1, 1.0f, false);
+    v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)d1, 1.0f, true);
+    return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// Sixteen int4 values (one dword pair of a lane's packed bytes) -> int8
+// operands multiplied by 16: low nibbles shifted up, high nibbles masked.
+__device__ __forceinline__ uint32_t int4_lo_x16(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t int4_hi_x16(uint32_t d) { return d & 0xF0F0F0F0u; }
+
+// ------------------------------------------------------------- epilogue
+
+struct Epilogue {
+    void* y;                 // [M, N] output
+    int64_t ldy;             // row stride of y in elements
+    int ydt;                 // OutDtype
+    const float* a_scale;    // fp8: one sA; w4a8: sA[M]; w8a16: unused
+    const float* w_scale;    // sW[0] or sW[N]
+    int w_per_channel;
+    const float* out_scale;  // E4M3 output only
+};
+
+__device__ __forceinline__ void store_out(const Epilogue& ep, int64_t m, int64_t n, float v) {
+    if (ep.ydt == OUT_F16) {
+        ((uint16_t*)ep.y)[m * ep.ldy + n] = (uint16_t)f32_to_f16_bits(v);
+    } else if (ep.ydt == OUT_BF16) {
+        ((uint16_t*)ep.y)[m * ep.ldy + n] = (uint16_t)f32_to_bf16_bits(v);
+    } else if (ep.ydt == OUT_F32) {
+        ((float*)ep.y)[m * ep.ldy + n] = v;
+    } else {  // OUT_E4M3
+        float t = v / *ep.out_scale;
+        ((uint8_t*)ep.y)[m * ep.ldy + n] = (uint8_t)e4m3_encode(t);
+    }
+}
+
+// Y = (sA * sW[n]) * acc for the fp8 linear; sW[n] * acc for W8A16 (sA = 1).
+__device__ __forceinline__ void epilogue_float(const Epilogue& ep, float sa, int64_t m, int64_t n, float acc) {
+    float sw = ep.w_scale[ep.w_per_channel ? n : 0];
+    float s = sa * sw;
+    store_out(ep, m, n, s * acc);
+}
+
+// W4A8: acc16 = sum Aq * (16 W4); acc = acc16 / 16 (exact); Y = (acc*sA[m])*sW[n].
+__device__ __forceinline__ void epilogue_int(const Epilogue& ep, int64_t m, int64_t n, int acc16) {
+    int acc = acc16 >> 4;
+    if (ep.ydt == OUT_I32) {
+        ((int32_t*)ep.y)[m * ep.ldy + n] = acc;
+        return;
+    }
+    float v = ((float)acc * ep.a_scale[m]) * ep.w_scale[n];
+    store_out(ep, m, n, v);
+}
+
+}  // namespace bql

@@ -1,0 +1,72 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Every launcher only enqueues work on `stream` and returns the HIP status
+// of the launch; argument checking happens before, in the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bql {
+
+// ---------------------------------------------------------------- quant.hip
+// Partial amax blocks used by the per-tensor reductions.
+int amax_blocks(int64_t numel);
+// Bytes of workspace the per-tensor quantizer needs (partials + scale).
+constexpr size_t QUANT_WS_BYTES = 8192;
+// Dynamic per-tensor E4M3 quantization.  ws holds the partials (first
+// 4096 bytes) and the scale (at byte 4096); scale_out may be null.
+hipError_t launch_quant_dynamic(const void* x, int xdt, int64_t numel, uint8_t* xq,
+                                float* scale_out, void* ws, hipStream_t stream);
+hipError_t launch_quant_static(const void* x, int xdt, int64_t numel, const float* scale,
+                               uint8_t* xq, hipStream_t stream);
+hipError_t launch_int8_per_token(const void* x, int xdt, int64_t M, int64_t K, int8_t* xq,
+                                 float* scales, hipStream_t stream);
+// amax over numel 16-bit values -> scale = amax / qmax (1 if amax == 0)
+// written to *scale; uses ws partials.
+hipError_t launch_tensor_scale(const void* x, int xdt, int64_t numel, float qmax,
+                               float* scale, void* ws, hipStream_t stream);
+
+// -------------------------------------------------------------- prepack.hip
+hipError_t launch_row_scales(const void* w, int wdt, int64_t N, int64_t K, float qmax,
+                             float* scales, hipStream_t stream);
+hipError_t launch_convert_scales(const void* s, int sdt, int64_t count, float* out,
+                                 hipStream_t stream);
+// wdt: 1 f16, 2 bf16, 4 e4m3 codes.  per_row selects scales[n] over scales[0].
+hipError_t launch_prepack_fp8(const void* w, int wdt, int64_t N, int64_t K, const float* scales,
+                              int per_row, uint8_t* packed, hipStream_t stream);
+hipError_t launch_prepack_int4(const uint8_t* w, int64_t N, int64_t K, uint8_t* packed,
+                               hipStream_t stream);
+hipError_t launch_unpack_fp8(const uint8_t* packed, int64_t N, int64_t K, uint8_t* out,
+                             hipStream_t stream);
+hipError_t launch_unpack_int4(const uint8_t* packed, int64_t N, int64_t K, uint8_t* out,
+                              hipStream_t stream);
+
+// ----------------------------------------------------------------- linears
+// V_FP8: E4M3 x E4M3 on the fp8 matrix cores (the hardware's fp8 dot
+//        accumulation); V_FP8X: E4M3 x E4M3 decoded losslessly to fp16 and
+//        summed exactly on the f16 matrix cores; V_W8A16: fp16 x E4M3 on the
+//        f16 matrix cores; V_W4A8: int8 x int4 on the int8 matrix cores.
+enum Variant { V_FP8 = 0, V_W8A16 = 1, V_W4A8 = 2, V_FP8X = 3 };
+
+struct LinearArgs {
+    int variant;
+    const void* a;          // fp8 codes / fp16 / int8, [M, K] row-major
+    const uint8_t* w;       // packed tiles
+    int64_t M, N, K;
+    // epilogue
+    void* y;
+    int ydt;
+    const float* a_scale;   // fp8: device scalar; w4a8: [M]
+    const float* w_scale;
+    int w_per_channel;
+    const float* out_scale;
+};
+
+// Workspace bytes the small-M (split-K) path may use at this shape.
+size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant);
+// Which path runs: true for the streaming small-M kernels.
+bool use_small_m(int variant, int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace bql

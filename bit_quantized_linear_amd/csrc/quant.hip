@@ -1,0 +1,222 @@
+// Activation quantizers for gfx950.
+//
+// Per-tensor dynamic E4M3 (vLLM PR #4118, "Algorithm": a new activation
+// scale every forward pass): scale = amax / 448, codes = E4M3(x / scale)
+// with an IEEE fp32 division, nearest-even rounding and saturation.  The
+// amax is a grid-wide dependency, so it takes two launches: per-block
+// partial maxima, then a cast kernel in which every block first folds the
+// (at most 1024) partials itself.  No atomics, no counters, nothing to
+// zero beforehand, and the result does not depend on the launch order.
+//
+// Per-token int8 for the W4A8 activations (QQQ issue #15, the answer on
+// online activation quantization): one block per row.
+#include "device.h"
+#include "kernels.h"
+
+namespace bql {
+
+constexpr int QT = 256;          // threads per block
+constexpr int MAX_PARTIALS = 1024;
+
+int amax_blocks(int64_t numel) {
+    int64_t vecs = (numel + 7) / 8;
+    int64_t b = (vecs + QT * 4 - 1) / (QT * 4);
+    if (b < 1) b = 1;
+    if (b > MAX_PARTIALS) b = MAX_PARTIALS;
+    return (int)b;
+}
+
+// Each block: max of |x| (as ordered magnitude bits) over a grid-stride
+// share of 8-element vectors; block 0 also takes the ragged tail.
+__global__ __launch_bounds__(QT) void amax_partial_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t numel,
+                                                          uint32_t* __restrict__ partial) {
+    __shared__ uint32_t sh[16];
+    const int64_t nvec = numel / 8;
+    const u4* xv = (const u4*)x;
+    uint32_t m = 0;
+    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * QT) {
+        u4 v = __builtin_nontemporal_load(&xv[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t lo = mag16(v[j] & 0xFFFFu), hi = mag16(v[j] >> 16);
+            m = m > lo ? m : lo;
+            m = m > hi ? m : hi;
+        }
+    }
+    if (blockIdx.x == 0) {
+        int64_t t = nvec * 8 + threadIdx.x;
+        if (t < numel) {
+            uint32_t e = mag16(x[t]);
+            m = m > e ? m : e;
+        }
+    }
+    m = block_max_u32(m, sh);
+    if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+template <int DT>
+__device__ __forceinline__ float scale_from_partials(const uint32_t* partial, int nparts,
+                                                     float qmax, uint32_t* sh) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = m > partial[i] ? m : partial[i];
+    m = block_max_u32(m, sh);
+    float amax = to_f32<DT>(m);
+    return amax == 0.0f ? 1.0f : amax / qmax;  // IEEE division
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+    return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
+// Cast kernel.  SCALE_FROM: 0 = fold amax partials, 1 = read a given scale.
+template <int DT, int SCALE_FROM>
+__global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restrict__ x,
+                                                       int64_t numel,
+                                                       const uint32_t* __restrict__ partial,
+                                                       int nparts,
+                                                       const float* __restrict__ given,
+                                                       uint8_t* __restrict__ xq,
+                                                       float* __restrict__ scale_out,
+                                                       float* __restrict__ scale_ws) {
+    __shared__ uint32_t sh[16];
+    float s;
+    if constexpr (SCALE_FROM == 0) {
+        s = scale_from_partials<DT>(partial, nparts, 448.0f, sh);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            if (scale_out) *scale_out = s;
+            if (scale_ws) *scale_ws = s;
+        }
+    } else {
+        s = *given;
+    }
+    const int64_t nvec = numel / 8;
+    const u4* xv = (const u4*)x;
+    u2* qv = (u2*)xq;
+    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * QT) {
+        u4 v = __builtin_nontemporal_load(&xv[i]);
+        uint32_t c[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            c[2 * j] = e4m3_encode(to_f32<DT>(v[j] & 0xFFFFu) / s);
+            c[2 * j + 1] = e4m3_encode(to_f32<DT>(v[j] >> 16) / s);
+        }
+        u2 o = {pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+        __builtin_nontemporal_store(o, &qv[i]);
+    }
+    if (blockIdx.x == 0) {
+        int64_t t = nvec * 8 + threadIdx.x;
+        if (t < numel) xq[t] = (uint8_t)e4m3_encode(to_f32<DT>(x[t]) / s);
+    }
+}
+
+// scale = amax / qmax over a whole tensor, for weight prepack.
+template <int DT>
+__global__ __launch_bounds__(QT) void finalize_scale_kernel(const uint32_t* __restrict__ partial,
+                                                            int nparts, float qmax,
+                                                            float* __restrict__ scale) {
+    __shared__ uint32_t sh[16];
+    float s = scale_from_partials<DT>(partial, nparts, qmax, sh);
+    if (threadIdx.x == 0) *scale = s;
+}
+
+static int cast_blocks(int64_t numel) {
+    int64_t vecs = (numel + 7) / 8;
+    int64_t b = (vecs + QT - 1) / QT;
+    if (b < 1) b = 1;
+    if (b > 8192) b = 8192;
+    return (int)b;
+}
+
+hipError_t launch_quant_dynamic(const void* x, int xdt, int64_t numel, uint8_t* xq,
+                                float* scale_out, void* ws, hipStream_t stream) {
+    uint32_t* partial = (uint32_t*)ws;
+    float* scale_ws = (float*)((char*)ws + 4096);
+    const int nb = amax_blocks(numel);
+    amax_partial_kernel<<<nb, QT, 0, stream>>>((const uint16_t*)x, numel, partial);
+    if (xdt == IN_BF16)
+        cast_e4m3_kernel<IN_BF16, 0><<<cast_blocks(numel), QT, 0, stream>>>(
+            (const uint16_t*)x, numel, partial, nb, nullptr, xq, scale_out, scale_ws);
+    else
+        cast_e4m3_kernel<IN_F16, 0><<<cast_blocks(numel), QT, 0, stream>>>(
+            (const uint16_t*)x, numel, partial, nb, nullptr, xq, scale_out, scale_ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_static(const void* x, int xdt, int64_t numel, const float* scale,
+                               uint8_t* xq, hipStream_t stream) {
+    if (xdt == IN_BF16)
+        cast_e4m3_kernel<IN_BF16, 1><<<cast_blocks(numel), QT, 0, stream>>>(
+            (const uint16_t*)x, numel, nullptr, 0, scale, xq, nullptr, nullptr);
+    else
+        cast_e4m3_kernel<IN_F16, 1><<<cast_blocks(numel), QT, 0, stream>>>(
+            (const uint16_t*)x, numel, nullptr, 0, scale, xq, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_tensor_scale(const void* x, int xdt, int64_t numel, float qmax,
+                               float* scale, void* ws, hipStream_t stream) {
+    uint32_t* partial = (uint32_t*)ws;
+    const int nb = amax_blocks(numel);
+    amax_partial_kernel<<<nb, QT, 0, stream>>>((const uint16_t*)x, numel, partial);
+    if (xdt == IN_BF16)
+        finalize_scale_kernel<IN_BF16><<<1, QT, 0, stream>>>(partial, nb, qmax, scale);
+    else
+        finalize_scale_kernel<IN_F16><<<1, QT, 0, stream>>>(partial, nb, qmax, scale);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- per-token int8
+
+template <int DT>
+__global__ __launch_bounds__(QT) void int8_per_token_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t K,
+                                                            int8_t* __restrict__ xq,
+                                                            float* __restrict__ scales) {
+    __shared__ uint32_t sh[16];
+    const int64_t m = blockIdx.x;
+    const u4* row = (const u4*)(x + m * K);
+    const int64_t nvec = K / 8;  // K is a multiple of 16
+    uint32_t mb = 0;
+    for (int64_t i = threadIdx.x; i < nvec; i += QT) {
+        u4 v = row[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t lo = mag16(v[j] & 0xFFFFu), hi = mag16(v[j] >> 16);
+            mb = mb > lo ? mb : lo;
+            mb = mb > hi ? mb : hi;
+        }
+    }
+    mb = block_max_u32(mb, sh);
+    const float amax = to_f32<DT>(mb);
+    const float s = amax == 0.0f ? 1.0f : amax / 127.0f;
+    if (threadIdx.x == 0) scales[m] = s;
+    u2* out = (u2*)(xq + m * K);
+    for (int64_t i = threadIdx.x; i < nvec; i += QT) {
+        u4 v = row[i];
+        uint32_t c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t b = (j & 1) ? (v[j >> 1] >> 16) : (v[j >> 1] & 0xFFFFu);
+            float t = __builtin_rintf(to_f32<DT>(b) / s);
+            t = t > 127.0f ? 127.0f : (t < -127.0f ? -127.0f : t);
+            c[j] = (uint32_t)(int32_t)t & 0xFFu;
+        }
+        out[i] = u2{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+    }
+}
+
+hipError_t launch_int8_per_token(const void* x, int xdt, int64_t M, int64_t K, int8_t* xq,
+                                 float* scales, hipStream_t stream) {
+    if (xdt == IN_BF16)
+        int8_per_token_kernel<IN_BF16><<<(unsigned)M, QT, 0, stream>>>((const uint16_t*)x, K, xq,
+                                                                        scales);
+    else
+        int8_per_token_kernel<IN_F16><<<(unsigned)M, QT, 0, stream>>>((const uint16_t*)x, K, xq,
+                                                                       scales);
+    return hipGetLastError();
+}
+
+}  // namespace bql

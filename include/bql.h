@@ -1,0 +1,245 @@
+/*
+ * bql.h - C ABI of the MI355X (gfx950) quantized-linear library.
+ *
+ * The operations are the ones the pages revolve around:
+ *   - dynamic per-tensor activation quantization to OCP FP8 E4M3, with a new
+ *     scale every forward pass (vLLM PR #4118 "[Kernel][FP8] Initial support
+ *     with dynamic per-tensor scaling", section "Algorithm"); the scale is
+ *     amax / 448 and the cast rounds to nearest even and saturates at +-448;
+ *   - weight quantization to E4M3 after load with a per-tensor scale (same
+ *     section), or a per-output-channel scale vector of length N
+ *     (optimum-quanto PR #241 "Marlin fp8", the kernel's b_scales check:
+ *     rank 2, shape (1, size_n));
+ *   - the FP8 GEMM Y = (scale_a * scale_w[n]) * (Aq . Wq^T) with fp32
+ *     accumulation (vLLM PR #4118, the torch._scaled_mm micro-benchmark),
+ *     with an fp16/bf16 output or an FP8 output quantized by a given
+ *     output_scale (vLLM discussion #5802 "RFC: FP8 Quantization Schema",
+ *     the answer on output_scale);
+ *   - weight-only fp8 (W8A16) linear with per-channel scales (optimum-quanto
+ *     PR #241);
+ *   - W4A8 per-channel integer linear: int4 weights widened to int8 by a
+ *     multiply by 16, int8 per-token activations, int32 accumulation, a
+ *     per-channel scale epilogue (QQQ issue #15 "Condition to achieve linear
+ *     speedup?").
+ *
+ * Conventions (all entry points):
+ *   - Every pointer is device memory owned by the caller unless marked
+ *     "host".  The library never allocates, never frees, never synchronizes
+ *     the host: all work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and completes asynchronously.
+ *   - Matrices are row-major and contiguous: A is [M,K], Y is [M,N], an
+ *     unpacked weight is [N,K] (the nn.Linear layout, Y = A . W^T).  No bias.
+ *   - N and K must be multiples of 16 (the FP8 GEMMs on the pages need
+ *     dimensions divisible by 16; vLLM discussion #5802, the gate_proj
+ *     question), else BQL_ERR_SHAPE.  M >= 0 is free; M = 0 is a no-op.
+ *   - Device pointers must be 16-byte aligned, else BQL_ERR_ALIGN.  With
+ *     M = 0 the activation, weight and output pointers are not examined.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is launched, the status is returned and a message is
+ *     kept for bql_last_error() (per thread).  A failure reported by the HIP
+ *     runtime at launch returns BQL_ERR_HIP.
+ *   - Workspaces are caller-owned device buffers of at least the size the
+ *     matching *_workspace_size() function returns; their content on entry
+ *     does not matter and is garbage on exit.  Calls that overlap in time
+ *     must not share a workspace.
+ *   - No entry point may be called concurrently with another call that
+ *     writes the same output buffers.
+ */
+#ifndef BQL_H
+#define BQL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQL_ABI_VERSION 1
+
+typedef enum bql_status {
+    BQL_OK = 0,
+    BQL_ERR_NULL = 1,      /* a required pointer is NULL */
+    BQL_ERR_DTYPE = 2,     /* unsupported dtype / format combination */
+    BQL_ERR_SHAPE = 3,     /* negative size, N or K not a multiple of 16, too large */
+    BQL_ERR_ALIGN = 4,     /* a device pointer is not 16-byte aligned */
+    BQL_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+    BQL_ERR_HIP = 6,       /* the HIP runtime reported an error */
+    BQL_ERR_ARG = 7        /* another invalid argument */
+} bql_status;
+
+typedef enum bql_dtype {
+    BQL_F16 = 1,   /* IEEE binary16 */
+    BQL_BF16 = 2,  /* bfloat16 */
+    BQL_F32 = 3,   /* IEEE binary32 */
+    BQL_E4M3 = 4,  /* OCP FP8 E4M3 (bias 7, max 448, S.1111.111 = NaN), one byte */
+    BQL_I8 = 5,    /* int8 */
+    BQL_I32 = 6,   /* int32 */
+    BQL_INT4 = 7   /* logical int4: two's complement nibbles, two per byte
+                      along K, the low nibble holding the even k */
+} bql_dtype;
+
+typedef enum bql_wfmt {
+    BQL_WFMT_FP8_TENSOR = 1,  /* E4M3 weight, one fp32 scale */
+    BQL_WFMT_FP8_CHANNEL = 2, /* E4M3 weight, fp32 scale per output channel n */
+    BQL_WFMT_INT4_CHANNEL = 3 /* int4 weight, fp32 scale per output channel n */
+} bql_wfmt;
+
+/* How the fp8 linear sums its products (torch._scaled_mm, which the vLLM
+ * PR #4118 micro-benchmark calls, has the same choice as use_fast_accum). */
+typedef enum bql_accum {
+    /* Every product dec(a)*dec(w) is formed exactly and summed in fp32:
+     * the codes are widened losslessly to fp16 and multiplied on the f16
+     * matrix cores (peak 2.5 PFLOP/s dense on MI355X). */
+    BQL_ACCUM_EXACT = 0,
+    /* The fp8 matrix-core instruction (peak 5 PFLOP/s dense).  On gfx950 it
+     * adds each run of 8 consecutive-k products in a fixed-point window about
+     * 14 bits wide aligned to the largest of the 8, then adds that partial
+     * into fp32: products more than ~2^6 below the largest of their run lose
+     * low-order bits (measured; error <= ~2^-12 of sum |products| per output). */
+    BQL_ACCUM_FAST = 1
+} bql_accum;
+
+typedef void* bql_stream; /* hipStream_t */
+
+/* ABI version compiled into the library (BQL_ABI_VERSION). */
+int bql_abi_version(void);
+
+/* Message of the last failed call made by this thread ("" if none). The
+ * string is owned by the library and valid until the next call on this
+ * thread. */
+const char* bql_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Activation quantization
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes for bql_fp8_quantize_dynamic over `numel` elements. */
+size_t bql_quantize_workspace_size(int64_t numel);
+
+/* Dynamic per-tensor quantization (vLLM PR #4118, "Algorithm"):
+ *   amax = max |x|,  scale = fp32(amax / 448)  (1.0 when amax is 0),
+ *   xq[i] = E4M3(fp32(x[i] / scale))  with an IEEE fp32 division, round to
+ *   nearest even, saturation to +-448 and the sign kept on zero.
+ * x: `numel` values of dtype xdt (BQL_F16 or BQL_BF16), any numel >= 0.
+ * xq: numel bytes.  scale_out: one fp32 in device memory (may be NULL).
+ * ws: >= bql_quantize_workspace_size(numel) bytes. */
+bql_status bql_fp8_quantize_dynamic(const void* x, bql_dtype xdt, int64_t numel,
+                                    uint8_t* xq, float* scale_out, void* ws,
+                                    size_t ws_bytes, bql_stream stream);
+
+/* Static (given-scale) quantization, the checkpoint input_scale of the
+ * vLLM FP8 quantization-schema RFC (static scaling):
+ *   xq[i] = E4M3(fp32(x[i] / *scale)).
+ * scale: one fp32 in device memory, must be positive and finite. */
+bql_status bql_fp8_quantize_static(const void* x, bql_dtype xdt, int64_t numel,
+                                   const float* scale, uint8_t* xq, bql_stream stream);
+
+/* Per-token symmetric int8 quantization of the W4A8 activations (QQQ issue
+ * #15, the answer on online activation quantization):
+ *   scale[m] = fp32(max_k |x[m,k]| / 127)  (1.0 for an all-zero row),
+ *   xq[m,k] = clamp(round_half_even(fp32(x[m,k] / scale[m])), -127, 127).
+ * x: [M,K] of dtype xdt (BQL_F16 or BQL_BF16); xq: [M,K] int8;
+ * scales: [M] fp32.  K must be a multiple of 16. */
+bql_status bql_int8_quantize_per_token(const void* x, bql_dtype xdt, int64_t M, int64_t K,
+                                       int8_t* xq, float* scales, bql_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Weight prepack (done once, after load)
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of the packed device layout for an [N,K] weight in format fmt
+ * (K is padded with zeros up to a multiple of 128 inside the layout). */
+size_t bql_packed_weight_bytes(int64_t N, int64_t K, bql_wfmt fmt);
+
+/* Workspace bytes for bql_prepack_weight. */
+size_t bql_prepack_workspace_size(int64_t N, int64_t K, bql_wfmt fmt);
+
+/* Quantize (if needed) and lay out a weight for the linear kernels (vLLM
+ * PR #4118: weight scale computed after load and stored with the weight;
+ * optimum-quanto PR #241: per-channel scales; QQQ issue #15: int4 packing).
+ *   w: [N,K] of dtype wdt:
+ *      BQL_F16 / BQL_BF16 with fmt FP8_TENSOR or FP8_CHANNEL;
+ *      BQL_E4M3 codes with fmt FP8_TENSOR or FP8_CHANNEL (scales_in needed);
+ *      BQL_INT4 (logical packing, N*K/2 bytes) with fmt INT4_CHANNEL
+ *      (scales_in needed).
+ *   scales_in: NULL, or 1 (FP8_TENSOR) / N (*_CHANNEL) scales of dtype sdt
+ *      (BQL_F16 or BQL_F32).  NULL with a float weight means
+ *      scale = fp32(amax / 448) over the whole tensor (FP8_TENSOR) or over
+ *      each row n (FP8_CHANNEL), 1.0 where the amax is 0.  The float weight
+ *      is then quantized as Wq = E4M3(fp32(W / scale)).
+ *   packed: bql_packed_weight_bytes(N, K, fmt) bytes, private layout.
+ *   scales_out: fp32, 1 (FP8_TENSOR) or N entries, in logical n order.
+ *   ws: >= bql_prepack_workspace_size(N, K, fmt) bytes. */
+bql_status bql_prepack_weight(const void* w, bql_dtype wdt, int64_t N, int64_t K,
+                              bql_wfmt fmt, const void* scales_in, bql_dtype sdt,
+                              void* packed, float* scales_out, void* ws, size_t ws_bytes,
+                              bql_stream stream);
+
+/* Inverse of the layout step of bql_prepack_weight: writes the logical
+ * weight codes, [N,K] E4M3 bytes for the FP8 formats or N*K/2 bytes of
+ * logical int4 for INT4_CHANNEL. */
+bql_status bql_unpack_weight(const void* packed, int64_t N, int64_t K, bql_wfmt fmt,
+                             void* out, bql_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Linears
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes for bql_fp8_linear at this shape. */
+size_t bql_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* FP8 linear (vLLM PR #4118; the torch._scaled_mm semantics):
+ *   Y[m,n] = (sA * sW[n]) * sum_k dec(Aq[m,k]) * dec(Wq[n,k]), fp32 accumulation
+ *   (exact products with BQL_ACCUM_EXACT).
+ *   a: [M,K].  adt = BQL_F16 or BQL_BF16: A is quantized dynamically per
+ *      tensor exactly as bql_fp8_quantize_dynamic does, and if a_scale is
+ *      not NULL the scale used is written there.  adt = BQL_E4M3: A already
+ *      holds codes and a_scale (required) holds sA.
+ *   w_packed/w_scale: from bql_prepack_weight in FP8_TENSOR (w_per_channel
+ *      = 0, one scale) or FP8_CHANNEL (w_per_channel = 1, N scales).
+ *   y: [M,N] of ydt: BQL_F16 / BQL_BF16 (round to nearest even of the fp32
+ *      value (sA*sW[n])*acc), BQL_F32 (that fp32 value itself), or
+ *      BQL_E4M3 with output_scale (required, one
+ *      positive fp32): Y codes = E4M3(fp32(Y / output_scale)) (vLLM
+ *      discussion #5802, output_scale).
+ *   accum: BQL_ACCUM_EXACT or BQL_ACCUM_FAST (see bql_accum).
+ *   ws: >= bql_fp8_linear_workspace_size(M, N, K) bytes. */
+bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale,
+                          const void* w_packed, const float* w_scale, int w_per_channel,
+                          int64_t M, int64_t N, int64_t K, const float* output_scale,
+                          void* y, bql_dtype ydt, bql_accum accum, void* ws, size_t ws_bytes,
+                          bql_stream stream);
+
+/* Workspace bytes for bql_w8a16_linear at this shape. */
+size_t bql_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Weight-only fp8 linear (optimum-quanto PR #241 "Marlin fp8"):
+ *   Y[m,n] = sW[n] * sum_k A[m,k] * dec(Wq[n,k]), fp32 accumulation.
+ *   a: [M,K] fp16.  w_packed: FP8_CHANNEL layout.  w_scales: N fp32.
+ *   y: [M,N] of ydt = BQL_F16, BQL_BF16 or BQL_F32. */
+bql_status bql_w8a16_linear(const void* a, const void* w_packed, const float* w_scales,
+                            int64_t M, int64_t N, int64_t K, void* y, bql_dtype ydt,
+                            void* ws, size_t ws_bytes, bql_stream stream);
+
+/* Workspace bytes for bql_w4a8_linear at this shape. */
+size_t bql_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* W4A8 per-channel integer linear (QQQ issue #15):
+ *   acc[m,n] = sum_k Aq[m,k] * W4[n,k] in int32 (the int4 values are used
+ *   as 16*W4 in the int8 MMA and the sum is divided by 16 exactly),
+ *   Y[m,n] = (fp32(acc) * sA[m]) * sW[n].
+ *   aq: [M,K] int8; a_scales: M fp32 (may be NULL when ydt = BQL_I32);
+ *   w_packed: INT4_CHANNEL layout; w_scales: N fp32 (may be NULL when
+ *   ydt = BQL_I32).  y: [M,N] of ydt = BQL_F16, BQL_BF16, BQL_F32 or BQL_I32
+ *   (the raw accumulator).  K <= 131072 keeps 16 * acc inside int32. */
+bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* w_packed,
+                           const float* w_scales, int64_t M, int64_t N, int64_t K,
+                           void* y, bql_dtype ydt, void* ws, size_t ws_bytes,
+                           bql_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQL_H */

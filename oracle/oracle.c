@@ -130,6 +130,7 @@ void bqo_quant_per_tensor(const float* x, int64_t n, uint8_t* q, float* scale_ou
     for (int64_t i = 0; i < n; ++i)
         if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
     float s = scale_from_amax(amax, 448.0f);
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         float r = x[i] / s;                     /* IEEE fp32 division */
         q[i] = bqo_e4m3_encode((double)r);

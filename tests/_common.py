@@ -1,0 +1,116 @@
+"""Helpers shared by the GPU parity tests: moving seeded host arrays to the
+device, sampling output rows, and the comparison rules.
+
+The comparison rules:
+  * integer/byte results (E4M3 codes, scales as bit patterns, int8 codes,
+    int32 accumulators) must be identical;
+  * float outputs must satisfy |got - ref| <= 5e-3 (|ref| + 1e-2 max|ref|)
+    against the oracle's fp64 result;
+  * an fp8 output code c is accepted when c = E4M3(v) for some v within
+    that tolerance of the oracle's Y / output_scale (fp32 accumulation
+    order decides codes near rounding boundaries).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as wl
+
+DEV = "cuda:0"
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def dev16(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    """uint16 bit patterns -> fp16/bf16 device tensor of the same shape."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(DEV).view(TORCH_DT[dtype])
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rows_for(M: int, seed: int, count: int = 32) -> np.ndarray:
+    """All rows when few, else first, last and a seeded sample."""
+    if M <= count:
+        return np.arange(M, dtype=np.int64)
+    g = np.random.Generator(np.random.PCG64(seed))
+    r = set(g.choice(M, size=count - 2, replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(r), dtype=np.int64)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, what: str):
+    ok, worst = oracle.within_tolerance(got, ref)
+    assert ok, f"{what}: worst |d|/bound = {worst:.3g}"
+    say(f"  {what}: worst |d|/bound = {worst:.3g}")
+
+
+def assert_fast_bound(got: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray, what: str):
+    """Bound for the fp8 matrix cores' own accumulation (fast mode).
+
+    Measured on gfx950: each run of 8 consecutive-k products is added in a
+    fixed-point window of 14 bit positions aligned to the exponent e of the
+    largest of the 8, so each of the other 7 loses less than 2^(e-13) <=
+    2^-13 * (largest) and a run errs by < 7 * 2^-13 * sum|p| < 2^-10 sum|p|.
+    abs_sum is sA sW[n] sum_k |dec(a) dec(w)| per output; on top comes the
+    output rounding, covered by the float tolerance."""
+    tol = 5e-3 * (np.abs(ref) + 1e-2 * np.abs(ref).max()) + 2.0 ** -10 * abs_sum
+    d = np.abs(got - ref)
+    worst = float((d / tol).max()) if d.size else 0.0
+    assert np.all(d <= tol), f"{what}: worst |d|/bound = {worst:.3g}"
+    say(f"  {what}: worst |d|/fast-bound = {worst:.3g}")
+
+
+def assert_fp8_out(codes: np.ndarray, v_ref: np.ndarray, what: str) -> float:
+    """Acceptance of fp8 output codes; returns the exact-match fraction."""
+    tab = oracle.e4m3_decode_table()
+    codes = codes.astype(np.int64)
+    assert not np.any((codes & 0x7F) == 0x7F), f"{what}: NaN code"
+    got = tab[codes]
+    tol = 5e-3 * (np.abs(v_ref) + 1e-2 * np.abs(v_ref).max())
+    lo = oracle.e4m3_encode_array(v_ref - tol)
+    hi = oracle.e4m3_encode_array(v_ref + tol)
+    lo_v, hi_v = tab[lo.astype(np.int64)], tab[hi.astype(np.int64)]
+    ok = (got >= lo_v) & (got <= hi_v)
+    assert ok.all(), f"{what}: {int((~ok).sum())} fp8 codes outside the tolerance window"
+    exact = float(np.mean(codes == oracle.e4m3_encode_array(v_ref).astype(np.int64)))
+    say(f"  {what}: fp8 codes exact match {exact:.4f}")
+    return exact
+
+
+class Weights:
+    """A seeded fp16/bf16 weight [N,K] with the oracle's quantization."""
+
+    def __init__(self, cfg: int, idx: int, N: int, K: int, dtype: str, per_channel: bool):
+        g = wl.rng(cfg, idx, 1)
+        self.N, self.K, self.dtype = N, K, dtype
+        self.bits = wl.weight(g, N, K, dtype)
+        wf = oracle.decode_input(self.bits, dtype)
+        if per_channel:
+            self.codes, self.scales = oracle.quant_per_row(wf)
+        else:
+            self.codes, s = oracle.quant_per_tensor(wf)
+            self.scales = np.array([s], dtype=np.float32)
+        del wf

@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/bql.h declares, and
+reject bad arguments on the host with the documented status before anything
+is launched.  None of these calls reaches a kernel: every one fails
+validation or is a pure size query, or has M = 0 (a no-op).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_linear_amd as bql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bql.h")
+
+OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_ARG = range(8)
+A16 = ctypes.c_void_p(0x10000)       # fake, aligned: never dereferenced on these paths
+MIS = ctypes.c_void_p(0x10008)       # fake, 8-byte aligned only
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bql_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bql.lib()
+
+
+def test_header_declares_the_binding_surface():
+    assert header_functions() == sorted(bql.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version(L):
+    assert L.bql_abi_version() == 1
+
+
+def test_packed_weight_bytes(L):
+    # 16 x 128 tiles; K padded up to a multiple of 128
+    assert L.bql_packed_weight_bytes(4096, 4096, 1) == 4096 * 4096
+    assert L.bql_packed_weight_bytes(4096, 4096, 2) == 4096 * 4096
+    assert L.bql_packed_weight_bytes(4096, 4096, 3) == 4096 * 4096 // 2
+    assert L.bql_packed_weight_bytes(48, 144, 1) == 3 * 2 * 2048
+    assert L.bql_packed_weight_bytes(48, 144, 3) == 3 * 2 * 1024
+    assert L.bql_packed_weight_bytes(0, 16, 1) == 0
+
+
+def test_workspace_sizes_are_monotone_and_cover_aq(L):
+    for (M, N, K) in [(1, 4096, 4096), (16, 1024, 1024), (1024, 28672, 4096), (4096, 8192, 28672)]:
+        ws = L.bql_fp8_linear_workspace_size(M, N, K)
+        assert ws >= 8192 + M * K
+        assert L.bql_w8a16_linear_workspace_size(M, N, K) % 256 == 0
+        assert L.bql_w4a8_linear_workspace_size(M, N, K) % 256 == 0
+    assert L.bql_fp8_linear_workspace_size(0, 16, 16) == 0
+    assert L.bql_quantize_workspace_size(123) >= 4096 + 4
+
+
+def _err(L):
+    return L.bql_last_error().decode()
+
+
+def test_fp8_linear_validation(L):
+    f = L.bql_fp8_linear
+    ws = L.bql_fp8_linear_workspace_size(4, 64, 64)
+    args = dict(a=A16, adt=2, sa=None, w=A16, ws_=A16, pc=0, M=4, N=64, K=64, os_=None,
+                y=A16, ydt=2, acc=0, work=A16, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["a"], a["adt"], a["sa"], a["w"], a["ws_"], a["pc"], a["M"], a["N"], a["K"],
+                 a["os_"], a["y"], a["ydt"], a["acc"], a["work"], a["wsb"], None)
+
+    assert call(a=None) == ERR_NULL and "a is NULL" in _err(L)
+    assert call(w=None) == ERR_NULL
+    assert call(y=None) == ERR_NULL
+    assert call(ws_=None) == ERR_NULL
+    assert call(a=MIS) == ERR_ALIGN
+    assert call(N=60) == ERR_SHAPE and "multiples of 16" in _err(L)
+    assert call(K=8) == ERR_SHAPE
+    assert call(M=-1) == ERR_SHAPE
+    assert call(M=(1 << 22) + 1) == ERR_SHAPE
+    assert call(adt=5) == ERR_DTYPE
+    assert call(ydt=6) == ERR_DTYPE
+    assert call(ydt=5) == ERR_DTYPE
+    assert call(pc=2) == ERR_ARG
+    assert call(acc=2) == ERR_ARG
+    assert call(adt=4) == ERR_NULL          # pre-quantized A needs a_scale
+    assert call(ydt=4) == ERR_NULL          # fp8 output needs output_scale
+    assert call(work=None) == ERR_WS
+    assert call(wsb=ws - 1) == ERR_WS
+    assert call(work=ctypes.c_void_p(0x10010)) == ERR_ALIGN  # workspace needs 256
+    assert call(M=0, wsb=0, work=None) == OK  # no-op
+
+
+def test_quantizer_validation(L):
+    q = L.bql_fp8_quantize_dynamic
+    assert q(None, 1, 10, A16, None, A16, 8192, None) == ERR_NULL
+    assert q(A16, 3, 10, A16, None, A16, 8192, None) == ERR_DTYPE
+    assert q(A16, 1, -1, A16, None, A16, 8192, None) == ERR_SHAPE
+    assert q(A16, 1, 10, A16, None, None, 0, None) == ERR_WS
+    assert q(A16, 1, 10, A16, None, A16, 100, None) == ERR_WS
+    assert q(A16, 1, 0, A16, None, A16, 8192, None) == OK
+    s = L.bql_fp8_quantize_static
+    assert s(A16, 2, 10, None, A16, None) == ERR_NULL
+    assert s(A16, 2, 0, A16, A16, None) == OK
+    p = L.bql_int8_quantize_per_token
+    assert p(A16, 1, 4, 24, A16, A16, None) == ERR_SHAPE
+    assert p(A16, 1, 4, 32, A16, None, None) == ERR_NULL
+    assert p(A16, 1, 0, 32, A16, A16, None) == OK
+
+
+def test_prepack_validation(L):
+    f = L.bql_prepack_weight
+    assert f(A16, 2, 64, 60, 1, None, 0, A16, A16, A16, 8192, None) == ERR_SHAPE
+    assert f(A16, 5, 64, 64, 1, None, 0, A16, A16, A16, 8192, None) == ERR_DTYPE
+    assert f(A16, 2, 64, 64, 9, None, 0, A16, A16, A16, 8192, None) == ERR_ARG
+    assert f(A16, 4, 64, 64, 1, None, 0, A16, A16, A16, 8192, None) == ERR_NULL  # codes need scales
+    assert f(A16, 2, 64, 64, 3, A16, 1, A16, A16, None, 0, None) == ERR_DTYPE    # int4 needs INT4
+    assert f(A16, 7, 64, 64, 3, None, 0, A16, A16, None, 0, None) == ERR_NULL    # int4 needs scales
+    assert f(A16, 2, 64, 64, 1, None, 0, A16, A16, None, 0, None) == ERR_WS      # per-tensor amax ws
+    assert f(A16, 2, 64, 64, 1, A16, 2, A16, A16, None, 0, None) == ERR_DTYPE    # bf16 scales refused
+    u = L.bql_unpack_weight
+    assert u(None, 64, 64, 1, A16, None) == ERR_NULL
+    assert u(A16, 64, 64, 7, A16, None) == ERR_ARG
+
+
+def test_w8a16_and_w4a8_validation(L):
+    f = L.bql_w8a16_linear
+    ws = L.bql_w8a16_linear_workspace_size(1, 64, 64)
+    assert f(A16, A16, A16, 1, 64, 64, A16, 4, A16, ws, None) == ERR_DTYPE
+    assert f(A16, A16, None, 1, 64, 64, A16, 1, A16, ws, None) == ERR_NULL
+    assert f(A16, A16, A16, 0, 64, 64, A16, 1, None, 0, None) == OK
+    g = L.bql_w4a8_linear
+    ws = L.bql_w4a8_linear_workspace_size(1, 64, 64)
+    assert g(A16, A16, A16, A16, 1, 64, 64, A16, 4, A16, ws, None) == ERR_DTYPE
+    assert g(A16, None, A16, A16, 1, 64, 64, A16, 1, A16, ws, None) == ERR_NULL
+    assert g(A16, A16, A16, A16, 1, 64, 131088, A16, 1, A16, ws, None) == ERR_SHAPE
+    assert g(A16, None, A16, None, 0, 64, 64, A16, 6, None, 0, None) == OK  # raw int32: scales optional
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        bql.quantize_dynamic(torch.zeros(16, dtype=torch.float16))
