@@ -1,0 +1,261 @@
+"""Benchmark of the quantized-linear hot path on one MI355X.
+
+Workload: the four Llama-3-8B-shaped W8A8 fp8 linears (N,K) = (6144,4096),
+(4096,4096), (28672,4096), (4096,14336) -- the layer shapes of the vLLM PR
+#4118 micro-benchmark -- with bf16 activations N(0,1) carrying 1% outlier
+channels x20, weights N(0,0.02) quantized per tensor to E4M3 once (offline,
+not timed), dynamic per-tensor activation quantization every call, exact
+fp32 accumulation and a bf16 output.
+
+One step = the whole hot path over one batch: for each of the four linears,
+the activation amax, the scale, the E4M3 cast and the fp8 GEMM with its
+scale epilogue (bql_fp8_linear, accum exact).  The headline value is the
+step's TFLOP/s at M = 1024 tokens; the M = 1 decode pass (the streaming
+small-M kernel with its split-K reduce) is timed the same way and reported
+in HBM GB/s of algorithmic bytes.  Weights rotate over enough copies that
+each pass touches more than twice the 256 MB Infinity Cache.
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+METRIC = "fp8 linear TFLOP/s at M=1024 + HBM GB/s at M=1, Llama-shaped N×K"
+PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_F16_TFLOPS = 2500.0
+SHAPES = wl.CFG3_SHAPES
+ROTATE_BYTES = 640 * 2 ** 20  # > 2 x 256 MiB Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(M, N, K):
+    """Wq (1 B/elem) + A bf16 + Y bf16 + the two scales."""
+    return N * K + 2 * M * K + 2 * M * N + 8
+
+
+def build_weights(bql, dev):
+    """Seeded host weights -> device, packed per tensor, rotated copies."""
+    host, packed = [], []
+    for idx, (N, K) in enumerate(SHAPES):
+        bits = wl.weight(wl.rng(3, idx, 1), N, K, "bf16")
+        host.append(bits)
+        w = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        pw = bql.prepack_weight(w, "fp8_tensor")
+        del w
+        packed.append(pw)
+    total = sum(N * K for N, K in SHAPES)
+    copies = max(1, -(-ROTATE_BYTES // total))
+    rot = [packed]
+    for _ in range(copies - 1):
+        rot.append([bql.PackedWeight(p.packed.clone(), p.scales.clone(), p.N, p.K, p.fmt)
+                    for p in packed])
+    return host, rot
+
+
+def build_activations(M, dev):
+    bits, dev_t = [], []
+    for idx, (N, K) in enumerate(SHAPES):
+        b = wl.activation(wl.rng(3, idx, M, 3), M, K, "bf16", "channels")
+        bits.append(b)
+        dev_t.append(torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16))
+    return bits, dev_t
+
+
+def time_steps(step, steps, warmup):
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def event_avg_us(launch, n):
+    """Average duration of `launch` over n back-to-back launches, HIP events
+    on torch's current stream (the stream the library launches on)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    launch(0)
+    e0.record(s)
+    for i in range(n):
+        launch(i)
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def cpu_baseline(host_w, act_bits, M, rows_per_shape):
+    """The CPU oracle on a bounded sample of the same M = 1024 step: every
+    activation tensor quantized in full, `rows_per_shape` output rows of each
+    linear computed; time scaled to all M rows (the quantization is counted
+    once, the dot products M / rows times)."""
+    import oracle
+    t_quant = t_dot = 0.0
+    flops = 0
+    rows = np.linspace(0, M - 1, rows_per_shape).astype(np.int64)
+    for (N, K), wbits, abits in zip(SHAPES, host_w, act_bits):
+        wq, sw = oracle.quant_per_tensor(oracle.decode_input(wbits, "bf16"))  # offline, untimed
+        t0 = time.perf_counter()
+        aq, sa = oracle.quant_per_tensor(oracle.decode_input(abits, "bf16"))
+        t1 = time.perf_counter()
+        oracle.fp8_linear(aq, sa, wq, sw, rows=rows)
+        t2 = time.perf_counter()
+        t_quant += t1 - t0
+        t_dot += t2 - t1
+        flops += 2 * M * N * K
+    est = t_quant + t_dot * (M / rows_per_shape)
+    return {"value": round(flops / est / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"all activations quantized; {rows_per_shape} of {M} output rows per linear "
+                      f"computed ({t_quant + t_dot:.1f} s), dot-product time scaled to {M} rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the dominant-kernel launches (for a rocprofv3 run of that kernel)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import bit_quantized_linear_amd as bql
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bql.lib()
+
+    log("generating weights ...")
+    host_w, rot = build_weights(bql, dev)
+    nrot = len(rot)
+
+    def run_pass(M, fast=False, prequant=False, timed=True):
+        abits, a = build_activations(M, dev)
+        outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N, K in SHAPES]
+        wss = [torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8,
+                           device=dev) for N, K in SHAPES]
+        pre = None
+        if prequant:
+            pre = [bql.quantize_dynamic(x) for x in a]
+            pre = [(q.view(torch.float8_e4m3fn), s) for q, s in pre]
+
+        def step(i):
+            ws_set = rot[i % nrot]
+            for j in range(len(SHAPES)):
+                if prequant:
+                    bql.fp8_linear(pre[j][0], ws_set[j], a_scale=pre[j][1], out_dtype=torch.bfloat16,
+                                   out=outs[j], ws=wss[j], fast_accum=fast)
+                else:
+                    bql.fp8_linear(a[j], ws_set[j], out_dtype=torch.bfloat16, out=outs[j],
+                                   ws=wss[j], fast_accum=fast)
+        sec = time_steps(step, args.steps, args.warmup) if timed else float("nan")
+        flops = sum(2 * M * N * K for N, K in SHAPES)
+        byts = sum(algorithmic_bytes(M, N, K) for N, K in SHAPES)
+        return abits, pre, outs, wss, sec, flops, byts
+
+    # ---- headline: M = 1024, exact accumulation, dynamic activation quant
+    M = 1024
+    if not args.roofline_only:
+        log("timing M=1024 exact ...")
+        abits, _, _, _, sec, flops, byts = run_pass(M)
+        value = flops / sec / 1e12
+
+    # dominant kernel: the tiled GEMM of the (28672, 4096) linear, pre-quantized A
+    def kernel_roofline(fast):
+        _, pre, outs, wss, _, _, _ = run_pass(M, fast=fast, prequant=True, timed=not args.roofline_only)
+        j = 2
+        N, K = SHAPES[j]
+
+        def launch(i):
+            bql.fp8_linear(pre[j][0], rot[i % nrot][j], a_scale=pre[j][1], out_dtype=torch.bfloat16,
+                           out=outs[j], ws=wss[j], fast_accum=fast)
+        us = event_avg_us(launch, 50)
+        fl = 2 * M * N * K
+        peak = PEAK_FP8_TFLOPS if fast else PEAK_F16_TFLOPS
+        ach = fl / us / 1e6
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None,
+                "kernel": f"gemm_kernel<{'V_FP8' if fast else 'V_FP8X'}> M={M} N={N} K={K}",
+                "avg_launch_us": round(us, 2), "flops_per_launch": fl}
+    log("kernel rooflines ...")
+    roof = kernel_roofline(False)
+    roof_fast = kernel_roofline(True)
+    if args.roofline_only:
+        print(json.dumps({"roofline": roof, "fast_accum_roofline": roof_fast}), flush=True)
+        return
+
+    # fast accumulation (fp8 matrix cores' own accumulation), same step
+    log("timing M=1024 fast ...")
+    _, _, _, _, sec_f, _, _ = run_pass(M, fast=True)
+
+    # ---- M = 1 decode pass
+    log("timing M=1 ...")
+    _, _, _, _, sec1, flops1, byts1 = run_pass(1)
+    _, _, _, _, sec1p, _, _ = run_pass(1, prequant=True)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3-8B-shaped W8A8 fp8 linears (N,K)=(6144,4096),(4096,4096),"
+                        "(28672,4096),(4096,14336); bf16 A N(0,1) with 1% outlier channels x20, "
+                        "dynamic per-tensor E4M3 activation scale, per-tensor E4M3 weights, "
+                        "exact fp32 accumulation, bf16 out",
+            "M": M, "accum": "exact", "weight_rotation_copies": nrot,
+        },
+        "m1": {
+            "value": round(byts1 / sec1 / 1e9, 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(byts1 / sec1 / 1e9 / PEAK_HBM_GBS, 4),
+            "ms_per_pass": round(sec1 * 1e3, 4),
+            "gemm_only_GBs": round(byts1 / sec1p / 1e9, 1),
+            "note": "M=1, four linears, dynamic quant included; gemm_only = pre-quantized A",
+        },
+        "fast_accum": {
+            "value": round(flops / sec_f / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(sec_f * 1e3, 4), "roofline": roof_fast,
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(host_w, abits, M, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,6 +55,8 @@ _F = ctypes.c_float
 
 
 def _declare(L):
+    L.bqo_threads.restype = ctypes.c_int
+    L.bqo_threads.argtypes = []
     L.bqo_e4m3_decode.restype = ctypes.c_double
     L.bqo_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.bqo_e4m3_encode.restype = ctypes.c_uint8
@@ -93,6 +95,11 @@ def _rows(rows, M):
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     assert rows.size == 0 or (rows.min() >= 0 and rows.max() < M)
     return rows
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().bqo_threads())
 
 
 # ------------------------------------------------------------------ scalars

@@ -38,10 +38,22 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define BQO_F16 1
 #define BQO_BF16 2
 #define BQO_F32 3
+
+/* Host threads the parallel loops below use. */
+int bqo_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- E4M3 */
 
