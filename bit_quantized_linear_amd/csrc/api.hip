@@ -201,10 +201,12 @@ bql_status bql_unpack_weight(const void* packed, int64_t N, int64_t K, bql_wfmt 
 
 // ---------------------------------------------------------------- linears
 
-// fp8 workspace: [quantizer partials + scale: 8 KiB][Aq: M*K][split-K partials]
+// fp8 workspace: [quantizer partials + scale: 8 KiB][Aq, packed operand
+// tiles][split-K partials]
 size_t bql_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return bql::QUANT_WS_BYTES + align256((size_t)M * K) + align256(bql::small_m_ws_bytes(M, N, K, bql::V_FP8));
+    return bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K)) +
+           align256(bql::small_m_ws_bytes(M, N, K, bql::V_FP8));
 }
 
 bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const void* w_packed,
@@ -214,6 +216,7 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     hipStream_t s = (hipStream_t)stream;
     CHECK(need_m(M));
     CHECK(need_nk(N, K));
+    if (K > (int64_t(1) << 22)) return fail(BQL_ERR_SHAPE, "K above 2^22");
     if (!is_f16ish(adt) && adt != BQL_E4M3) return fail(BQL_ERR_DTYPE, "A must be BQL_F16, BQL_BF16 or BQL_E4M3");
     if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_E4M3)
         return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16, BQL_F32 or BQL_E4M3");
@@ -230,15 +233,16 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     CHECK(need_ws(ws, ws_bytes, bql_fp8_linear_workspace_size(M, N, K)));
 
     char* wsb = (char*)ws;
-    const uint8_t* aq = (const uint8_t*)a;
+    uint8_t* aq = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);
     const float* sa = a_scale;
+    hipError_t e;
     if (adt != BQL_E4M3) {
-        uint8_t* aq_ws = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);
-        hipError_t e = bql::launch_quant_dynamic(a, adt, M * K, aq_ws, a_scale, wsb, s);
-        if (e != hipSuccess) return hip_status(e);
-        aq = aq_ws;
+        e = bql::launch_quant_dynamic_packed(a, adt, M, K, aq, a_scale, wsb, s);
         sa = (const float*)(wsb + 4096);
+    } else {
+        e = bql::launch_pack_codes((const uint8_t*)a, M, K, aq, s);
     }
+    if (e != hipSuccess) return hip_status(e);
     bql::LinearArgs la;
     la.variant = accum == BQL_ACCUM_FAST ? bql::V_FP8 : bql::V_FP8X;
     la.a = aq;
@@ -252,7 +256,7 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     la.w_scale = w_scale;
     la.w_per_channel = w_per_channel;
     la.out_scale = output_scale;
-    char* part = wsb + bql::QUANT_WS_BYTES + align256((size_t)M * K);
+    char* part = wsb + bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K));
     return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_FP8), s));
 }
 
@@ -291,9 +295,10 @@ bql_status bql_w8a16_linear(const void* a, const void* w_packed, const float* w_
     return hip_status(bql::launch_linear(la, ws, ws_bytes, (hipStream_t)stream));
 }
 
+// W4A8 workspace: [Aq, packed operand tiles][split-K partials]
 size_t bql_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return align256(bql::small_m_ws_bytes(M, N, K, bql::V_W4A8));
+    return align256(bql::packed_act_bytes(M, K)) + align256(bql::small_m_ws_bytes(M, N, K, bql::V_W4A8));
 }
 
 bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* w_packed,
@@ -313,9 +318,12 @@ bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* 
         CHECK(need_ptr(w_scales, "w_scales"));
     }
     CHECK(need_ws(ws, ws_bytes, bql_w4a8_linear_workspace_size(M, N, K)));
+    uint8_t* aq_ws = (uint8_t*)ws;
+    hipError_t e = bql::launch_pack_codes((const uint8_t*)aq, M, K, aq_ws, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
     bql::LinearArgs la;
     la.variant = bql::V_W4A8;
-    la.a = aq;
+    la.a = aq_ws;
     la.w = (const uint8_t*)w_packed;
     la.M = M;
     la.N = N;
@@ -326,7 +334,9 @@ bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* 
     la.w_scale = w_scales;
     la.w_per_channel = 1;
     la.out_scale = nullptr;
-    return hip_status(bql::launch_linear(la, ws, ws_bytes, (hipStream_t)stream));
+    char* part = (char*)ws + align256(bql::packed_act_bytes(M, K));
+    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_W4A8),
+                                         (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -18,6 +18,15 @@ constexpr size_t QUANT_WS_BYTES = 8192;
 // 4096 bytes) and the scale (at byte 4096); scale_out may be null.
 hipError_t launch_quant_dynamic(const void* x, int xdt, int64_t numel, uint8_t* xq,
                                 float* scale_out, void* ws, hipStream_t stream);
+// Bytes of the packed 8-bit activation layout (16 x 128 operand tiles).
+size_t packed_act_bytes(int64_t M, int64_t K);
+// Dynamic per-tensor E4M3 of a row-major [M, K] activation, written in the
+// packed layout the linear kernels read.
+hipError_t launch_quant_dynamic_packed(const void* x, int xdt, int64_t M, int64_t K, uint8_t* xq,
+                                       float* scale_out, void* ws, hipStream_t stream);
+// Row-major 8-bit codes [M, K] (E4M3 or int8) -> packed layout.
+hipError_t launch_pack_codes(const uint8_t* src, int64_t M, int64_t K, uint8_t* dst,
+                             hipStream_t stream);
 hipError_t launch_quant_static(const void* x, int xdt, int64_t numel, const float* scale,
                                uint8_t* xq, hipStream_t stream);
 hipError_t launch_int8_per_token(const void* x, int xdt, int64_t M, int64_t K, int8_t* xq,

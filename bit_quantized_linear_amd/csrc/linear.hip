@@ -5,21 +5,27 @@
 // Two regimes, as the micro-benchmark on vLLM PR #4118 shows (small token
 // counts are a weight-streaming problem, large ones a matrix-core problem):
 //   * small M (<= 16 rows of A): a streaming kernel.  Each wave walks k-tiles
-//     of one or more 16-channel weight strips, loading every MFMA operand
-//     straight from HBM with 16-byte loads (the packed layout makes one
-//     wave-wide load 1 KiB contiguous), A rows padded to 16 by zero lanes.
-//     Waves of a block split K and are summed through LDS in a fixed order;
-//     blocks may split K further, with partials summed in a fixed order by
-//     a second kernel.  Deterministic, no atomics.
-//   * large M: a block-tiled MFMA kernel with both operands staged through
-//     LDS in operand order, double buffered, fused scale epilogue.
+//     of a 16-channel weight strip, loading every MFMA operand straight from
+//     HBM with 16-byte loads (the packed layout makes one wave-wide load
+//     1 KiB contiguous), A rows padded to 16.  Waves of a block split K and
+//     are summed through LDS in a fixed order; blocks may split K further,
+//     with partials summed in a fixed order by a second kernel.
+//     Deterministic, no atomics.
+//   * large M: a block-tiled MFMA kernel.  Both operands live in HBM in the
+//     MFMA operand tile layout (weights by prepack, 8-bit activations by
+//     the quantizer or a repack), so each 1 KiB of a stage is one
+//     buffer_load ... lds instruction that writes LDS directly (no VGPR
+//     staging, no address scatter).  A ring of S stages keeps S-1 k-tiles
+//     in flight; waits on the vector-memory counter are explicit because the
+//     compiler does not track these LDS writes.  The epilogue converts and
+//     stages each 16-row band through LDS and writes it with 16-byte stores.
 #include "device.h"
 #include "kernels.h"
 
 namespace bql {
 
 struct LinParams {
-    const void* a;
+    const void* a;          // packed 8-bit A (fp8 / int8 variants) or row-major fp16 (W8A16)
     const uint8_t* w;
     int64_t M, N, K, KT;
     int64_t kt_per_split;
@@ -58,21 +64,25 @@ template <> struct VT<V_W4A8> {
     using E = int;
 };
 
-// One lane's A operand for one k-tile: row `row`, k0 .. k0+31 (k0 = 128 kt
-// + 32 g for lane group g), zero where the row or k does not exist.
+// One lane's A operand for k-tile kt of row tile mt.  Packed 8-bit A: the
+// lane's 32 bytes are at tile + lane*16 and tile + 1024 + lane*16.  W8A16:
+// row-major fp16, row `row`, k0 .. k0+31 with k0 = 128 kt + 32 (lane/16),
+// zero where the row or k does not exist.
 template <int V>
-__device__ __forceinline__ void load_a(u4 (&f)[VT<V>::A_CHUNKS], const void* A, int64_t row,
-                                       bool ok, int64_t K, int64_t k0) {
+__device__ __forceinline__ void load_a(u4 (&f)[VT<V>::A_CHUNKS], const LinParams& p, int64_t mt,
+                                       int64_t kt, int lane, bool ok) {
     if constexpr (V == V_W8A16) {
-        const uint16_t* p = (const uint16_t*)A + row * K + k0;
+        const int64_t row = mt * 16 + (lane & 15);
+        const int64_t k0 = kt * TILE_K + 32 * (lane >> 4);
+        const uint16_t* q = (const uint16_t*)p.a + row * p.K + k0;
+        ok = ok && row < p.M;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            f[c] = (ok && k0 + 8 * c < K) ? *(const u4*)(p + 8 * c) : u4{0, 0, 0, 0};
+            f[c] = (ok && k0 + 8 * c < p.K) ? *(const u4*)(q + 8 * c) : u4{0, 0, 0, 0};
     } else {
-        const uint8_t* p = (const uint8_t*)A + row * K + k0;
+        const uint8_t* t = (const uint8_t*)p.a + (mt * p.KT + kt) * 2048 + lane * 16;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-            f[c] = (ok && k0 + 16 * c < K) ? *(const u4*)(p + 16 * c) : u4{0, 0, 0, 0};
+        for (int c = 0; c < 2; ++c) f[c] = ok ? *(const u4*)(t + 1024 * c) : u4{0, 0, 0, 0};
     }
 }
 
@@ -85,37 +95,51 @@ __device__ __forceinline__ void load_b(u4 (&f)[VT<V>::B_CHUNKS], const uint8_t* 
                   : u4{0, 0, 0, 0};
 }
 
+__device__ __forceinline__ v8i as_v8i(const u4& x0, const u4& x1) {
+    return v8i{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+               (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+}
+
+__device__ __forceinline__ v4i as_v4i(const u4& x) {
+    return v4i{(int)x[0], (int)x[1], (int)x[2], (int)x[3]};
+}
+
+// A lane's 32 E4M3 codes (k0 .. k0+31) as four fp16 operands of 8.
+__device__ __forceinline__ void decode32(const u4& x0, const u4& x1, v8h (&h)[4]) {
+    h[0] = e4m3x8_to_f16(x0[0], x0[1]);
+    h[1] = e4m3x8_to_f16(x0[2], x0[3]);
+    h[2] = e4m3x8_to_f16(x1[0], x1[1]);
+    h[3] = e4m3x8_to_f16(x1[2], x1[3]);
+}
+
+__device__ __forceinline__ void mma_w4a8(v4i& acc, const u4& alo, const u4& ahi, const u4& b) {
+    const v4i blo = {(int)int4_lo_x16(b[0]), (int)int4_lo_x16(b[1]),
+                     (int)int4_lo_x16(b[2]), (int)int4_lo_x16(b[3])};
+    const v4i bhi = {(int)int4_hi_x16(b[0]), (int)int4_hi_x16(b[1]),
+                     (int)int4_hi_x16(b[2]), (int)int4_hi_x16(b[3])};
+    acc = mfma_i8(as_v4i(alo), blo, acc);
+    acc = mfma_i8(as_v4i(ahi), bhi, acc);
+}
+
 template <int V>
 __device__ __forceinline__ void mma(typename VT<V>::Acc& acc, const u4 (&a)[VT<V>::A_CHUNKS],
                                     const u4 (&b)[VT<V>::B_CHUNKS]) {
     if constexpr (V == V_FP8) {
-        v8i av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
-                  (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
-        v8i bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
-                  (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
-        acc = mfma_fp8(av, bv, acc);
+        acc = mfma_fp8(as_v8i(a[0], a[1]), as_v8i(b[0], b[1]), acc);
     } else if constexpr (V == V_W4A8) {
-        v4i alo = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3]};
-        v4i ahi = {(int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
-        v4i blo = {(int)int4_lo_x16(b[0][0]), (int)int4_lo_x16(b[0][1]),
-                   (int)int4_lo_x16(b[0][2]), (int)int4_lo_x16(b[0][3])};
-        v4i bhi = {(int)int4_hi_x16(b[0][0]), (int)int4_hi_x16(b[0][1]),
-                   (int)int4_hi_x16(b[0][2]), (int)int4_hi_x16(b[0][3])};
-        acc = mfma_i8(alo, blo, acc);
-        acc = mfma_i8(ahi, bhi, acc);
+        mma_w4a8(acc, a[0], a[1], b[0]);
     } else if constexpr (V == V_FP8X) {
         // four f16 MFMAs over k0+8q .. k0+8q+7 on losslessly decoded codes
-        const uint32_t da[8] = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
-        const uint32_t db[8] = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
+        v8h ah[4], bh[4];
+        decode32(a[0], a[1], ah);
+        decode32(b[0], b[1], bh);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            acc = mfma_f16(e4m3x8_to_f16(da[2 * q], da[2 * q + 1]),
-                           e4m3x8_to_f16(db[2 * q], db[2 * q + 1]), acc);
-    } else {  // W8A16: four f16 MFMAs over k0+8q .. k0+8q+7
-        const uint32_t db[8] = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
+        for (int q = 0; q < 4; ++q) acc = mfma_f16(ah[q], bh[q], acc);
+    } else {  // W8A16: A is fp16 already
+        v8h bh[4];
+        decode32(b[0], b[1], bh);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            acc = mfma_f16(__builtin_bit_cast(v8h, a[q]), e4m3x8_to_f16(db[2 * q], db[2 * q + 1]), acc);
+        for (int q = 0; q < 4; ++q) acc = mfma_f16(__builtin_bit_cast(v8h, a[q]), bh[q], acc);
     }
 }
 
@@ -124,6 +148,29 @@ __device__ __forceinline__ void finish(const LinParams& p, float sa, int64_t m, 
                                        typename VT<V>::E v) {
     if constexpr (V == V_W4A8) epilogue_int(p.ep, m, n, v);
     else epilogue_float(p.ep, sa, m, n, v);
+}
+
+// Output value of one accumulator as the output dtype's bits (same
+// arithmetic as epilogue_float / epilogue_int).
+template <int V>
+__device__ __forceinline__ uint32_t out_bits(const Epilogue& ep, float sa, int64_t m, int64_t n,
+                                             typename VT<V>::E v) {
+    float y;
+    if constexpr (V == V_W4A8) {
+        const int acc = v >> 4;
+        if (ep.ydt == OUT_I32) return (uint32_t)acc;
+        y = ((float)acc * ep.a_scale[m]) * ep.w_scale[n];
+    } else {
+        y = (sa * ep.w_scale[ep.w_per_channel ? n : 0]) * v;
+    }
+    if (ep.ydt == OUT_F16) return f32_to_f16_bits(y);
+    if (ep.ydt == OUT_BF16) return f32_to_bf16_bits(y);
+    if (ep.ydt == OUT_F32) return __float_as_uint(y);
+    return e4m3_encode(y / *ep.out_scale);
+}
+
+__device__ __forceinline__ int out_size(int ydt) {
+    return ydt == OUT_E4M3 ? 1 : ((ydt == OUT_F32 || ydt == OUT_I32) ? 4 : 2);
 }
 
 // --------------------------------------------------------------- small M
@@ -139,8 +186,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
     const int64_t mt = blockIdx.z;
     const int64_t kt_begin = split * p.kt_per_split;
     const int64_t kt_end = kt_begin + p.kt_per_split < p.KT ? kt_begin + p.kt_per_split : p.KT;
-    const int64_t row = mt * 16 + (lane & 15);
-    const bool row_ok = row < p.M;
     const int g = lane >> 4;
 
     Acc acc[NT];
@@ -154,7 +199,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
         for (int u = 0; u < U; ++u) {
             const int64_t k = kt + u * WAVES;
             const bool kv = k < kt_end;
-            load_a<V>(a[u], p.a, row, row_ok && kv, p.K, k * TILE_K + 32 * g);
+            load_a<V>(a[u], p, mt, k, lane, kv);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
                 load_b<V>(b[u][j], p.w + ((nt0 + j) * p.KT + k) * BT, lane,
@@ -214,53 +259,78 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(LinParams p) {
 
 // --------------------------------------------------------------- large M
 
-template <int V, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_kernel(LinParams p) {
+// s_waitcnt vmcnt(N) that leaves the other counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int V, int BM, int BN, int WM, int WN, int S>
+struct GemmCfg {
+    static constexpr int NW = WM * WN;
+    static constexpr int BT = VT<V>::B_TILE;
+    static constexpr int A_BYTES = (BM / 16) * 2048;
+    static constexpr int B_BYTES = (BN / 16) * BT;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = S * STAGE;
+    static constexpr int FM = BM / (16 * WM), FN = BN / (16 * WN);
+    static constexpr int A_LD = A_BYTES / 1024, B_LD = B_BYTES / 1024;  // 1 KiB loads per stage
+    static constexpr int LDPW = (A_LD + B_LD) / NW;
+    static_assert(A_LD % NW == 0 && B_LD % NW == 0, "stage loads must split evenly over waves");
+    static_assert(LDPW * (S - 1) < 64, "vmcnt range");
+    // epilogue scratch: one 16-row band of a wave's tile, 4 bytes per value, padded rows
+    static constexpr int EPI_ROW = FN * 16 * 4 + 16;
+    static constexpr int EPI_WAVE = 16 * EPI_ROW;
+    static_assert(EPI_WAVE * NW <= LDS, "epilogue scratch must fit in the stage buffers");
+};
+
+template <int V, int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(LinParams p) {
+    using C = GemmCfg<V, BM, BN, WM, WN, S>;
     using Acc = typename VT<V>::Acc;
-    constexpr int BT = VT<V>::B_TILE;
-    constexpr int ASUB = BM / TILE_N, BSUB = BN / TILE_N;
-    constexpr int A_BYTES = ASUB * 2048;  // 8-bit A: a 16 x 128 sub-tile is 2 KiB
-    constexpr int B_BYTES = BSUB * BT;
-    constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int FM = BM / 32, FN = BN / 32;  // 2 x 2 waves, 16 x 16 fragments
-    constexpr int A_PER_T = A_BYTES / 16 / 256, B_PER_T = B_BYTES / 16 / 256;
-    static_assert(A_PER_T * 256 * 16 == A_BYTES && B_PER_T * 256 * 16 == B_BYTES, "tile split");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    constexpr int NW = C::NW, FM = C::FM, FN = C::FN, BT = C::BT;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-    const int64_t nt0 = n0 / TILE_N, ntiles = p.N / TILE_N;
-    const uint8_t* A = (const uint8_t*)p.a;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t nbn = (p.N + BN - 1) / BN;
+    const int64_t bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
+    const int64_t m0 = bm * BM, n0 = bn * BN;
+    const int64_t mt0 = m0 / 16, nt0 = n0 / 16;
+    const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
+    const int KT = (int)p.KT;
 
-    u4 ra[A_PER_T], rb[B_PER_T];
-    auto gload = [&](int64_t kt) {
+    // Buffer descriptors over this block's own strips; loads past them
+    // (rows beyond M, channels beyond N) return zeros.
+    const int64_t a_strips = mtiles - mt0 < BM / 16 ? mtiles - mt0 : BM / 16;
+    const int64_t b_strips = ntiles - nt0 < BN / 16 ? ntiles - nt0 : BN / 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.a + mt0 * p.KT * 2048), (short)0, (int)(a_strips * p.KT * 2048),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + nt0 * p.KT * BT), (short)0, (int)(b_strips * p.KT * BT), 0x00020000);
+
+    auto issue = [&](int kt, int stage) {
+        uint8_t* base = lds + stage * C::STAGE;
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-            const int64_t gm = m0 + r, gk = kt * TILE_K + c * 16;
-            ra[i] = (gm < p.M && gk < p.K) ? *(const u4*)(A + gm * p.K + gk) : u4{0, 0, 0, 0};
+        for (int i = 0; i < C::A_LD / NW; ++i) {
+            const int slot = wave + NW * i, sub = slot >> 1, h = slot & 1;
+            const int off = (sub * KT + kt) * 2048 + h * 1024 + lane * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + slot * 1024), 16, off, 0,
+                                                     0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            const int q = tid + 256 * i, j = q / (BT / 16), w = q % (BT / 16);
-            rb[i] = (nt0 + j < ntiles)
-                        ? __builtin_nontemporal_load((const u4*)(p.w + ((nt0 + j) * p.KT + kt) * BT + w * 16))
-                        : u4{0, 0, 0, 0};
-        }
-    };
-    auto sstore = [&](int buf) {
-        uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-            const int off = (r >> 4) * 2048 + (c & 1) * 1024 + ((r & 15) + 16 * (c >> 1)) * 16;
-            *(u4*)(base + off) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            const int q = tid + 256 * i;
-            *(u4*)(base + A_BYTES + q * 16) = rb[i];
+        for (int i = 0; i < C::B_LD / NW; ++i) {
+            const int slot = wave + NW * i;
+            int off;
+            if constexpr (BT == 2048) off = ((slot >> 1) * KT + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
+            else off = (slot * KT + kt) * 1024 + lane * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + C::A_BYTES + slot * 1024),
+                                                     16, off, 0, 0, 0);
         }
     };
 
@@ -270,49 +340,104 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinParams p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < p.KT; ++kt) {
-        const int cur = (int)(kt & 1);
-        const bool more = kt + 1 < p.KT;
-        if (more) gload(kt + 1);
-        const uint8_t* base = lds + cur * STAGE;
-        u4 af[FM][2];
-        u4 bf[FN][VT<V>::B_CHUNKS];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const uint8_t* t = base + (wm * FM + i) * 2048 + lane * 16;
-            af[i][0] = *(const u4*)t;
-            af[i][1] = *(const u4*)(t + 1024);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const uint8_t* t = base + A_BYTES + (wn * FN + j) * BT + lane * 16;
-#pragma unroll
-            for (int c = 0; c < VT<V>::B_CHUNKS; ++c) bf[j][c] = *(const u4*)(t + c * 1024);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) mma<V>(acc[i][j], af[i], bf[j]);
-        if (more) sstore(cur ^ 1);
-        __syncthreads();
-    }
+    for (int s = 0; s < S - 1; ++s)
+        if (s < KT) issue(s, s);
 
-    const float sa = (V == V_FP8 || V == V_FP8X) ? *p.ep.a_scale : 1.0f;
+    for (int kt = 0; kt < KT; ++kt) {
+        // This wave's loads of stage kt are done once no more than the loads
+        // of the stages issued after it are outstanding.
+        const int after = (KT - 1 - kt) < (S - 2) ? (KT - 1 - kt) : (S - 2);
+        if (after == S - 2) wait_vmcnt<C::LDPW * (S - 2)>();
+        else if (S > 3 && after == 1) wait_vmcnt<C::LDPW>();
+        else if (S > 4 && after == 2) wait_vmcnt<C::LDPW * 2>();
+        else wait_vmcnt<0>();
+        // every wave's share of stage kt is in LDS, and every wave has
+        // finished reading the stage that the next issue overwrites
+        __syncthreads();
+        if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+
+        const uint8_t* base = lds + (kt % S) * C::STAGE;
+        const uint8_t* abase = base + (wm * FM) * 2048 + lane * 16;
+        const uint8_t* bbase = base + C::A_BYTES + (wn * FN) * BT + lane * 16;
+        if constexpr (V == V_FP8) {
+            v8i bf[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+            for (int j = 0; j < FN; ++j)
+                bf[j] = as_v8i(*(const u4*)(bbase + j * BT), *(const u4*)(bbase + j * BT + 1024));
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + (wn * FN + j) * 16 + (lane & 15);
-            if (n >= p.N) continue;
+            for (int i = 0; i < FM; ++i) {
+                const v8i af =
+                    as_v8i(*(const u4*)(abase + i * 2048), *(const u4*)(abase + i * 2048 + 1024));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + (wm * FM + i) * 16 + 4 * (lane >> 4) + r;
-                if (m < p.M) finish<V>(p, sa, m, n, acc[i][j][r]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8(af, bf[j], acc[i][j]);
+            }
+        } else if constexpr (V == V_FP8X) {
+            v8h bh[FN][4];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                decode32(*(const u4*)(bbase + j * BT), *(const u4*)(bbase + j * BT + 1024), bh[j]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                v8h ah[4];
+                decode32(*(const u4*)(abase + i * 2048), *(const u4*)(abase + i * 2048 + 1024), ah);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[i][j] = mfma_f16(ah[q], bh[j][q], acc[i][j]);
+            }
+        } else {  // V_W4A8
+            u4 bf[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = *(const u4*)(bbase + j * BT);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const u4 alo = *(const u4*)(abase + i * 2048);
+                const u4 ahi = *(const u4*)(abase + i * 2048 + 1024);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mma_w4a8(acc[i][j], alo, ahi, bf[j]);
             }
         }
+    }
+
+    // ---- epilogue: per wave, per 16-row band: convert, stage in LDS, 16-byte stores
+    __syncthreads();  // all waves are done with the stage buffers
+    const float sa = (V == V_FP8 || V == V_FP8X) ? *p.ep.a_scale : 1.0f;
+    const int esz = out_size(p.ep.ydt);
+    uint8_t* scratch = lds + wave * C::EPI_WAVE;
+    const int chunks_per_row = FN * 16 * esz / 16;
+    const int64_t col0 = n0 + wn * FN * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t rbase = m0 + (wm * FM + i) * 16;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int c = j * 16 + (lane & 15);
+            const int64_t n = col0 + c;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * (lane >> 4) + r;
+                const uint32_t bits = (n < p.N && rbase + row < p.M)
+                                          ? out_bits<V>(p.ep, sa, rbase + row, n, acc[i][j][r])
+                                          : 0u;
+                uint8_t* d = scratch + row * C::EPI_ROW + c * esz;
+                if (esz == 4) *(uint32_t*)d = bits;
+                else if (esz == 2) *(uint16_t*)d = (uint16_t)bits;
+                else *d = (uint8_t)bits;
+            }
+        }
+        // the band is written and read back by this wave only
+        __builtin_amdgcn_wave_barrier();
+        for (int q = lane; q < 16 * chunks_per_row; q += 64) {
+            const int row = q / chunks_per_row, ch = q % chunks_per_row;
+            const int64_t m = rbase + row;
+            const int64_t n = col0 + (int64_t)ch * 16 / esz;
+            if (m < p.M && n < p.N)
+                *(u4*)((uint8_t*)p.ep.y + (m * p.ep.ldy + n) * esz) =
+                    *(const u4*)(scratch + row * C::EPI_ROW + ch * 16);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 // ------------------------------------------------------------------ host
@@ -362,12 +487,22 @@ static hipError_t run_gemv(LinParams p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int V>
-static hipError_t run_gemm(LinParams p, hipStream_t stream) {
-    constexpr int BM = 128, BN = 128;
-    dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-    gemm_kernel<V, BM, BN><<<grid, 256, 0, stream>>>(p);
+template <int V, int BM, int BN, int WM, int WN, int S>
+static hipError_t launch_gemm(const LinParams& p, hipStream_t stream) {
+    using C = GemmCfg<V, BM, BN, WM, WN, S>;
+    const void* fn = (const void*)gemm_kernel<V, BM, BN, WM, WN, S>;
+    // the dynamic LDS above 64 KiB needs the attribute; setting it is cheap
+    // and idempotent, so it is set on every launch (any device, any thread)
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    gemm_kernel<V, BM, BN, WM, WN, S><<<(unsigned)blocks, 64 * WM * WN, C::LDS, stream>>>(p);
     return hipGetLastError();
+}
+
+template <int V>
+static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
+    return launch_gemm<V, 128, 128, 2, 2, 2>(p, stream);
 }
 
 hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -16,7 +16,7 @@
 namespace bql {
 
 constexpr int QT = 256;          // threads per block
-constexpr int MAX_PARTIALS = 1024;
+constexpr int MAX_PARTIALS = 256;
 
 int amax_blocks(int64_t numel) {
     int64_t vecs = (numel + 7) / 8;
@@ -35,8 +35,22 @@ __global__ __launch_bounds__(QT) void amax_partial_kernel(const uint16_t* __rest
     const int64_t nvec = numel / 8;
     const u4* xv = (const u4*)x;
     uint32_t m = 0;
-    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
-         i += (int64_t)gridDim.x * QT) {
+    const int64_t stride = (int64_t)gridDim.x * QT;
+    int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight per thread
+        u4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&xv[i + u * stride]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t lo = mag16(v[u][j] & 0xFFFFu), hi = mag16(v[u][j] >> 16);
+                m = m > lo ? m : lo;
+                m = m > hi ? m : hi;
+            }
+    }
+    for (; i < nvec; i += stride) {
         u4 v = __builtin_nontemporal_load(&xv[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -110,6 +124,97 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
         int64_t t = nvec * 8 + threadIdx.x;
         if (t < numel) xq[t] = (uint8_t)e4m3_encode(to_f32<DT>(x[t]) / s);
     }
+}
+
+// ------------------------------------------------ packed 8-bit activations
+//
+// The linear kernels read 8-bit activations in the MFMA operand tile layout
+// the weights use: tiles of 16 rows x 128 k (2048 B), all k-tiles of a
+// 16-row strip consecutive, a tile stored as [half h][lane l][16 B] with
+// row l % 16 and k = 32*(l/16) + 16*h + j.  Columns k >= K up to the tile
+// edge hold zero codes; rows past M in the last strip are never stored to
+// an output and are left unwritten.
+
+__device__ __forceinline__ int64_t packed_offset(int64_t m, int64_t k, int64_t KT) {
+    return ((m >> 4) * KT + (k >> 7)) * 2048 + ((k >> 4) & 1) * 1024 +
+           ((m & 15) + 16 * ((k >> 5) & 3)) * 16 + (k & 15);
+}
+
+// Grid-stride over items of 8 consecutive k of one row (KT*16 items per
+// row, the padding up to the tile edge included).
+template <int DT>
+__global__ __launch_bounds__(QT) void cast_e4m3_packed_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t M, int64_t K, int64_t KT,
+                                                              const uint32_t* __restrict__ partial,
+                                                              int nparts, uint8_t* __restrict__ xq,
+                                                              float* __restrict__ scale_out,
+                                                              float* __restrict__ scale_ws) {
+    __shared__ uint32_t sh[16];
+    const float s = scale_from_partials<DT>(partial, nparts, 448.0f, sh);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (scale_out) *scale_out = s;
+        if (scale_ws) *scale_ws = s;
+    }
+    const int64_t per_row = KT * 16, total = M * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < total; i += (int64_t)gridDim.x * QT) {
+        const int64_t m = i / per_row, k = (i % per_row) * 8;
+        uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (k < K) {  // K is a multiple of 16: the 8 values are all inside or all padding
+            const u4 v = __builtin_nontemporal_load((const u4*)(x + m * K + k));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[2 * j] = e4m3_encode(to_f32<DT>(v[j] & 0xFFFFu) / s);
+                c[2 * j + 1] = e4m3_encode(to_f32<DT>(v[j] >> 16) / s);
+            }
+        }
+        *(u2*)(xq + packed_offset(m, k, KT)) =
+            u2{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+    }
+}
+
+// Row-major 8-bit codes [M, K] -> packed layout; grid-stride over 16-byte
+// items (KT*8 per row, the padding up to the tile edge included).
+__global__ __launch_bounds__(QT) void pack_codes_kernel(const uint8_t* __restrict__ src, int64_t M,
+                                                        int64_t K, int64_t KT,
+                                                        uint8_t* __restrict__ dst) {
+    const int64_t per_row = KT * 8, total = M * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < total; i += (int64_t)gridDim.x * QT) {
+        const int64_t m = i / per_row, k = (i % per_row) * 16;
+        const u4 v = k < K ? *(const u4*)(src + m * K + k) : u4{0, 0, 0, 0};
+        *(u4*)(dst + packed_offset(m, k, KT)) = v;
+    }
+}
+
+size_t packed_act_bytes(int64_t M, int64_t K) {
+    return (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128) * 2048;
+}
+
+hipError_t launch_quant_dynamic_packed(const void* x, int xdt, int64_t M, int64_t K, uint8_t* xq,
+                                       float* scale_out, void* ws, hipStream_t stream) {
+    uint32_t* partial = (uint32_t*)ws;
+    float* scale_ws = (float*)((char*)ws + 4096);
+    const int64_t numel = M * K;
+    const int nb = amax_blocks(numel);
+    amax_partial_kernel<<<nb, QT, 0, stream>>>((const uint16_t*)x, numel, partial);
+    const int64_t KT = (K + 127) / 128;
+    int64_t blocks = (M * KT * 16 + QT - 1) / QT;
+    if (blocks > 8192) blocks = 8192;
+    if (xdt == IN_BF16)
+        cast_e4m3_packed_kernel<IN_BF16><<<(unsigned)blocks, QT, 0, stream>>>(
+            (const uint16_t*)x, M, K, KT, partial, nb, xq, scale_out, scale_ws);
+    else
+        cast_e4m3_packed_kernel<IN_F16><<<(unsigned)blocks, QT, 0, stream>>>(
+            (const uint16_t*)x, M, K, KT, partial, nb, xq, scale_out, scale_ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_codes(const uint8_t* src, int64_t M, int64_t K, uint8_t* dst,
+                             hipStream_t stream) {
+    const int64_t KT = (K + 127) / 128;
+    int64_t blocks = (M * KT * 8 + QT - 1) / QT;
+    if (blocks > 8192) blocks = 8192;
+    pack_codes_kernel<<<(unsigned)blocks, QT, 0, stream>>>(src, M, K, KT, dst);
+    return hipGetLastError();
 }
 
 // scale = amax / qmax over a whole tensor, for weight prepack.

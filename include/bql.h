@@ -204,6 +204,7 @@ size_t bql_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
  *      positive fp32): Y codes = E4M3(fp32(Y / output_scale)) (vLLM
  *      discussion #5802, output_scale).
  *   accum: BQL_ACCUM_EXACT or BQL_ACCUM_FAST (see bql_accum).
+ *   K <= 2^22.
  *   ws: >= bql_fp8_linear_workspace_size(M, N, K) bytes. */
 bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale,
                           const void* w_packed, const float* w_scale, int w_per_channel,
