@@ -234,6 +234,29 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
 
     char* wsb = (char*)ws;
     uint8_t* aq = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);
+    char* part = wsb + bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K));
+    const int variant = accum == BQL_ACCUM_FAST ? bql::V_FP8 : bql::V_FP8X;
+    if (adt != BQL_E4M3 && bql::fused_small_m(M, N, K)) {
+        // one launch: the small-M kernel quantizes A itself
+        bql::LinearArgs la;
+        la.variant = variant;
+        la.a = a;
+        la.w = (const uint8_t*)w_packed;
+        la.M = M;
+        la.N = N;
+        la.K = K;
+        la.y = y;
+        la.ydt = ydt;
+        la.a_scale = nullptr;
+        la.w_scale = w_scale;
+        la.w_per_channel = w_per_channel;
+        la.out_scale = output_scale;
+        la.fused = 1;
+        la.xdt = adt;
+        la.scale_out = a_scale;
+        la.scale_ws = (float*)(wsb + 4096);
+        return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+    }
     const float* sa = a_scale;
     hipError_t e;
     if (adt != BQL_E4M3) {
@@ -244,7 +267,7 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     }
     if (e != hipSuccess) return hip_status(e);
     bql::LinearArgs la;
-    la.variant = accum == BQL_ACCUM_FAST ? bql::V_FP8 : bql::V_FP8X;
+    la.variant = variant;
     la.a = aq;
     la.w = (const uint8_t*)w_packed;
     la.M = M;
@@ -256,8 +279,7 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     la.w_scale = w_scale;
     la.w_per_channel = w_per_channel;
     la.out_scale = output_scale;
-    char* part = wsb + bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K));
-    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_FP8), s));
+    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
 }
 
 size_t bql_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {

@@ -70,7 +70,15 @@ struct LinearArgs {
     const float* w_scale;
     int w_per_channel;
     const float* out_scale;
+    // fused small-M fp8: A is row-major fp16/bf16 and is quantized in-kernel
+    int fused = 0;
+    int xdt = 0;
+    float* scale_out = nullptr;  // optional copy of sA for the caller
+    float* scale_ws = nullptr;   // sA in the workspace (read by the split-K reduce)
 };
+
+// Whether an fp8 call with dynamic quantization runs the fused small-M kernel.
+bool fused_small_m(int64_t M, int64_t N, int64_t K);
 
 // Workspace bytes the small-M (split-K) path may use at this shape.
 size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant);

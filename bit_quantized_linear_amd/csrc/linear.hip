@@ -19,19 +19,25 @@
 //     in flight; waits on the vector-memory counter are explicit because the
 //     compiler does not track these LDS writes.  The epilogue converts and
 //     stages each 16-row band through LDS and writes it with 16-byte stores.
+#include <atomic>
+
 #include "device.h"
 #include "kernels.h"
 
 namespace bql {
 
 struct LinParams {
-    const void* a;          // packed 8-bit A (fp8 / int8 variants) or row-major fp16 (W8A16)
+    const void* a;          // packed 8-bit A (fp8 / int8 variants) or row-major fp16 (W8A16);
+                            // row-major fp16/bf16 when the small-M kernel quantizes A itself
     const uint8_t* w;
     int64_t M, N, K, KT;
     int64_t kt_per_split;
     int splits;
     void* partial;
     Epilogue ep;
+    int xdt;                // fused quantization: IN_F16 / IN_BF16
+    float* scale_out;       // fused quantization: optional copy of sA for the caller
+    float* scale_ws;        // fused quantization: sA for the split-K reduce
 };
 
 template <int V> struct VT;
@@ -175,10 +181,15 @@ __device__ __forceinline__ int out_size(int ydt) {
 
 // --------------------------------------------------------------- small M
 
-template <int V, int NT, int WAVES, int U>
+// FUSED (fp8 variants, M <= 4): the kernel quantizes A itself.  Every block
+// reads all of A for the per-tensor amax (a max, so every block gets the
+// same scale bit for bit), then casts the A slice its K split needs into
+// LDS as [M][slice] codes.  One launch instead of amax, cast and GEMV.
+template <int V, int NT, int WAVES, int U, bool FUSED>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
     using Acc = typename VT<V>::Acc;
     constexpr int BT = VT<V>::B_TILE;
+    extern __shared__ __attribute__((aligned(16))) uint8_t aq_lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t ntiles = p.N / TILE_N;
     const int64_t nt0 = (int64_t)blockIdx.x * NT;
@@ -188,27 +199,100 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
     const int64_t kt_end = kt_begin + p.kt_per_split < p.KT ? kt_begin + p.kt_per_split : p.KT;
     const int g = lane >> 4;
 
+    // Weight tiles for k-tiles kt, kt + WAVES, ... (U of them) of this wave.
+    auto load_batch = [&](int64_t kt, u4 (&b)[U][NT][VT<V>::B_CHUNKS]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = kt + u * WAVES;
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                load_b<V>(b[u][j], p.w + ((nt0 + j) * p.KT + k) * BT, lane,
+                          k < kt_end && (nt0 + j) < ntiles);
+        }
+    };
+    // The first batch of weights is requested before anything else, so its
+    // HBM latency overlaps the scale computation and the A cast below.
+    u4 bq[U][NT][VT<V>::B_CHUNKS];
+    load_batch(kt_begin + wave, bq);
+
+    float sa = 1.0f;
+    if constexpr (FUSED) {
+        __shared__ uint32_t sh[16];
+        const uint16_t* x = (const uint16_t*)p.a;
+        const int64_t nvec = p.M * p.K / 8;  // K is a multiple of 16
+        uint32_t mb = 0;
+        for (int64_t i = threadIdx.x; i < nvec; i += 64 * WAVES) {
+            const u4 v = ((const u4*)x)[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = mag16(v[j] & 0xFFFFu), hi = mag16(v[j] >> 16);
+                mb = mb > lo ? mb : lo;
+                mb = mb > hi ? mb : hi;
+            }
+        }
+        mb = block_max_u32(mb, sh);
+        const float amax = p.xdt == IN_BF16 ? to_f32<IN_BF16>(mb) : to_f32<IN_F16>(mb);
+        sa = amax == 0.0f ? 1.0f : amax / 448.0f;  // IEEE division, as the standalone quantizer
+        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+            if (p.scale_out) *p.scale_out = sa;
+            if (p.scale_ws) *p.scale_ws = sa;
+        }
+        const int64_t slice = p.kt_per_split * TILE_K, k_lo = kt_begin * TILE_K;
+        const int64_t items = p.M * slice / 8;
+        for (int64_t i = threadIdx.x; i < items; i += 64 * WAVES) {
+            const int64_t m = i / (slice / 8), kk = (i % (slice / 8)) * 8, k = k_lo + kk;
+            uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (k < p.K) {
+                const u4 v = *(const u4*)(x + m * p.K + k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = v[j] & 0xFFFFu, hi = v[j] >> 16;
+                    c[2 * j] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)) / sa);
+                    c[2 * j + 1] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)) / sa);
+                }
+            }
+            *(u2*)(aq_lds + m * slice + kk) = u2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                                 c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+        }
+        __syncthreads();
+    } else if constexpr (V == V_FP8 || V == V_FP8X) {
+        sa = *p.ep.a_scale;
+    }
+
     Acc acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = Acc{0, 0, 0, 0};
 
+    // Register double buffering: the next batch is in flight while this
+    // one is multiplied.
     for (int64_t kt = kt_begin + wave; kt < kt_end; kt += WAVES * U) {
+        u4 bn[U][NT][VT<V>::B_CHUNKS];
+        if (kt + WAVES * U < kt_end) load_batch(kt + WAVES * U, bn);
         u4 a[U][VT<V>::A_CHUNKS];
-        u4 b[U][NT][VT<V>::B_CHUNKS];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = kt + u * WAVES;
             const bool kv = k < kt_end;
-            load_a<V>(a[u], p, mt, k, lane, kv);
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-                load_b<V>(b[u][j], p.w + ((nt0 + j) * p.KT + k) * BT, lane,
-                          kv && (nt0 + j) < ntiles);
+            if constexpr (FUSED) {
+                const int row = lane & 15;
+                const uint8_t* t = aq_lds + row * p.kt_per_split * TILE_K + (k - kt_begin) * TILE_K + 32 * g;
+                const bool ok = kv && row < p.M;
+                a[u][0] = ok ? *(const u4*)t : u4{0, 0, 0, 0};
+                a[u][1] = ok ? *(const u4*)(t + 16) : u4{0, 0, 0, 0};
+            } else {
+                load_a<V>(a[u], p, mt, k, lane, kv);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) mma<V>(acc[j], a[u], b[u][j]);
+            for (int j = 0; j < NT; ++j) mma<V>(acc[j], a[u], bq[u][j]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int c = 0; c < VT<V>::B_CHUNKS; ++c) bq[u][j][c] = bn[u][j][c];
     }
 
     if constexpr (WAVES > 1) {
@@ -225,7 +309,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
         }
     }
 
-    const float sa = (V == V_FP8 || V == V_FP8X) ? *p.ep.a_scale : 1.0f;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         if (nt0 + j >= ntiles) continue;
@@ -442,10 +525,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(LinParams p) {
 
 // ------------------------------------------------------------------ host
 
-constexpr int GEMV_WAVES = 8;
 constexpr int GEMV_U = 2;
 constexpr int MAX_SPLITS = 8;
 constexpr int SMALL_M = 16;
+constexpr int FUSED_M = 4;                 // small-M fp8 calls that quantize A in-kernel
+constexpr int64_t FUSED_LDS = 48 * 1024;   // bytes of A codes a fused block may stage
 
 bool use_small_m(int variant, int64_t M, int64_t N, int64_t K) {
     (void)N; (void)K;
@@ -455,16 +539,21 @@ bool use_small_m(int variant, int64_t M, int64_t N, int64_t K) {
 struct GemvPlan {
     int64_t KT, kt_per_split;
     int splits;
+    int waves;
 };
 
+// Enough waves in flight to cover HBM latency: about 16 per CU, each with
+// GEMV_U weight tiles outstanding.  Few 16-channel strips get 16 waves per
+// block before K is split across blocks.
 static GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
     GemvPlan pl;
     pl.KT = (K + TILE_K - 1) / TILE_K;
-    const int64_t groups = N / TILE_N;
-    const int64_t mtiles = (M + 15) / 16;
+    const int64_t groups = (N / TILE_N) * ((M + 15) / 16);
+    pl.waves = (groups >= 1024 || pl.KT < 32) ? 8 : 16;
     int s = 1;
     if (M <= SMALL_M)
-        while (groups * mtiles * s < 1024 && s * 2 <= MAX_SPLITS && pl.KT / (s * 2) >= 2) s *= 2;
+        while (groups * s * pl.waves < 4096 && s * 2 <= MAX_SPLITS && pl.KT / (s * 2) >= pl.waves / 2)
+            s *= 2;
     pl.kt_per_split = (pl.KT + s - 1) / s;
     pl.splits = (int)((pl.KT + pl.kt_per_split - 1) / pl.kt_per_split);
     return pl;
@@ -476,10 +565,20 @@ size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant) {
     return pl.splits > 1 ? (size_t)pl.splits * M * N * 4 : 0;
 }
 
-template <int V>
-static hipError_t run_gemv(LinParams p, hipStream_t stream) {
+bool fused_small_m(int64_t M, int64_t N, int64_t K) {
+    if (M > FUSED_M) return false;
+    GemvPlan pl = plan_gemv(M, N, K);
+    return M * pl.kt_per_split * TILE_K <= FUSED_LDS;
+}
+
+template <int V, bool FUSED>
+static hipError_t run_gemv(LinParams p, int waves, hipStream_t stream) {
     dim3 grid((unsigned)(p.N / TILE_N), (unsigned)p.splits, (unsigned)((p.M + 15) / 16));
-    gemv_kernel<V, 1, GEMV_WAVES, GEMV_U><<<grid, 64 * GEMV_WAVES, 0, stream>>>(p);
+    const size_t lds = FUSED ? (size_t)(p.M * p.kt_per_split * TILE_K) : 0;
+    if (waves == 16)
+        gemv_kernel<V, 1, 16, GEMV_U, FUSED><<<grid, 64 * 16, lds, stream>>>(p);
+    else
+        gemv_kernel<V, 1, 8, GEMV_U, FUSED><<<grid, 64 * 8, lds, stream>>>(p);
     if (p.splits > 1) {
         const int64_t total = p.M * p.N;
         splitk_reduce_kernel<V><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
@@ -490,11 +589,19 @@ static hipError_t run_gemv(LinParams p, hipStream_t stream) {
 template <int V, int BM, int BN, int WM, int WN, int S>
 static hipError_t launch_gemm(const LinParams& p, hipStream_t stream) {
     using C = GemmCfg<V, BM, BN, WM, WN, S>;
-    const void* fn = (const void*)gemm_kernel<V, BM, BN, WM, WN, S>;
-    // the dynamic LDS above 64 KiB needs the attribute; setting it is cheap
-    // and idempotent, so it is set on every launch (any device, any thread)
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    // Dynamic LDS above 64 KiB needs the attribute, set once per device
+    // (before any graph capture can happen: the first launch is eager).
+    static std::atomic<uint64_t> configured{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (!(configured.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute((const void*)gemm_kernel<V, BM, BN, WM, WN, S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (e != hipSuccess) return e;
+        configured.fetch_or(bit, std::memory_order_acq_rel);
+    }
     const int64_t blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     gemm_kernel<V, BM, BN, WM, WN, S><<<(unsigned)blocks, 64 * WM * WN, C::LDS, stream>>>(p);
     return hipGetLastError();
@@ -521,16 +628,24 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
     p.ep.w_per_channel = args.w_per_channel;
     p.ep.out_scale = args.out_scale;
     p.partial = ws;
+    p.xdt = args.xdt;
+    p.scale_out = args.scale_out;
+    p.scale_ws = args.scale_ws;
     if (use_small_m(args.variant, args.M, args.N, args.K)) {
         GemvPlan pl = plan_gemv(args.M, args.N, args.K);
         p.KT = pl.KT;
         p.kt_per_split = pl.kt_per_split;
         p.splits = pl.splits;
+        if (args.fused) {
+            p.ep.a_scale = args.scale_ws;  // read by the split-K reduce
+            if (args.variant == V_FP8) return run_gemv<V_FP8, true>(p, pl.waves, stream);
+            return run_gemv<V_FP8X, true>(p, pl.waves, stream);
+        }
         switch (args.variant) {
-            case V_FP8: return run_gemv<V_FP8>(p, stream);
-            case V_FP8X: return run_gemv<V_FP8X>(p, stream);
-            case V_W8A16: return run_gemv<V_W8A16>(p, stream);
-            default: return run_gemv<V_W4A8>(p, stream);
+            case V_FP8: return run_gemv<V_FP8, false>(p, pl.waves, stream);
+            case V_FP8X: return run_gemv<V_FP8X, false>(p, pl.waves, stream);
+            case V_W8A16: return run_gemv<V_W8A16, false>(p, pl.waves, stream);
+            default: return run_gemv<V_W4A8, false>(p, pl.waves, stream);
         }
     }
     p.KT = (args.K + TILE_K - 1) / TILE_K;

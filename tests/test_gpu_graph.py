@@ -1,0 +1,79 @@
+"""Captured HIP graphs of the linears replay to the eager result.
+
+Every path is captured once (small-M fused and split-K, the tiled kernel,
+exact and fast accumulation, W8A16, W4A8) and replayed several times with
+eager work and synchronizations in between; each replay must equal the
+eager output bit for bit (all kernels are deterministic).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from _common import DEV, dev, dev16
+
+import bit_quantized_linear_amd as bql
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match(run, out, noise):
+    run()
+    torch.cuda.synchronize()
+    want = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up off the capture stream, as torch recommends
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(3):
+        out.zero_()
+        noise()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), want.view(torch.uint8))
+
+
+@pytest.mark.parametrize("fast", [False, True])
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (3, 1024, 1024), (16, 1024, 1024), (8, 4096, 4096),
+                                   (1024, 4096, 4096), (130, 272, 400)])
+def test_fp8_linear_graph(M, N, K, fast):
+    g = wl.rng(11, M, N)
+    pw = bql.prepack_weight(dev16(wl.weight(g, N, K, "bf16"), "bf16"), "fp8_tensor")
+    a = dev16(wl.activation(g, M, K, "bf16", "channels"), "bf16")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=DEV)
+    scale = torch.empty(1, dtype=torch.float32, device=DEV)
+    other = torch.empty_like(out)
+
+    def run():
+        bql.fp8_linear(a, pw, a_scale=scale, out_dtype=torch.bfloat16, out=out, ws=ws, fast_accum=fast)
+
+    def noise():  # eager work on the same library between replays
+        bql.fp8_linear(a * 2, pw, out_dtype=torch.bfloat16, out=other, fast_accum=fast)
+
+    _replays_match(run, out, noise)
+
+
+def test_w8a16_and_w4a8_graph():
+    g = wl.rng(12, 0)
+    N = K = 1024
+    pw16 = bql.prepack_weight(dev16(wl.weight(g, N, K, "f16"), "f16"), "fp8_channel")
+    a16 = dev16(wl.activation(g, 8, K, "f16"), "f16")
+    out16 = torch.empty((8, N), dtype=torch.float16, device=DEV)
+    _replays_match(lambda: bql.w8a16_linear(a16, pw16, out=out16), out16,
+                   lambda: bql.w8a16_linear(a16 * 3, pw16))
+    w4 = wl.int4_weight(g, N, K)
+    pw4 = bql.prepack_weight(dev(wl.pack_int4(w4).reshape(N, K // 2)), "int4_channel",
+                             scales=dev16(wl.w4a8_channel_scales(g, N), "f16"))
+    aq = dev(g.integers(-127, 128, (200, K), dtype=np.int8))
+    out4 = torch.empty((200, N), dtype=torch.int32, device=DEV)
+    ws4 = torch.empty(max(256, bql.lib().bql_w4a8_linear_workspace_size(200, N, K)), dtype=torch.uint8,
+                      device=DEV)
+    _replays_match(lambda: bql.w4a8_linear(aq, None, pw4, out_dtype=torch.int32, out=out4, ws=ws4), out4,
+                   lambda: bql.w4a8_linear(aq, None, pw4, out_dtype=torch.int32))
