@@ -352,6 +352,33 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also
+// drains every outstanding global load (vmcnt 0), which would retire the
+// LDS-DMA stages still in flight behind the one being waited for; the
+// DMA stages are waited for explicitly with wait_vmcnt instead.
+__device__ __forceinline__ void lds_barrier() {
+    // lgkmcnt(0): this wave's LDS reads have returned (vmcnt, expcnt left open)
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+}
+
+// Output tile of hardware block b. Blocks are dispatched to the 8 XCDs in
+// turn (block b to XCD b % 8) and each XCD has its own L2, so each XCD is
+// given one contiguous range of tiles; within it tiles run in groups of
+// GROUP_M tile rows, row index fastest, so that the blocks resident at the
+// same time on an XCD share A and W strips (read once into its L2, then hit).
+constexpr int XCDS = 8, GROUP_M = 8;
+__device__ __forceinline__ void tile_coords(int64_t b, int64_t nbm, int64_t nbn, int64_t& bm, int64_t& bn) {
+    const int64_t tiles = nbm * nbn, q = tiles / XCDS, r = tiles % XCDS;
+    const int64_t x = b % XCDS, j = b / XCDS;
+    const int64_t t = x * q + (x < r ? x : r) + j;
+    const int64_t group = t / (GROUP_M * nbn), first = group * GROUP_M;
+    const int64_t gm = nbm - first < GROUP_M ? nbm - first : GROUP_M;
+    const int64_t rem = t - group * GROUP_M * nbn;
+    bm = first + rem % gm;
+    bn = rem / gm;
+}
+
 template <int V, int BM, int BN, int WM, int WN, int S>
 struct GemmCfg {
     static constexpr int NW = WM * WN;
@@ -380,8 +407,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(LinParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t nbn = (p.N + BN - 1) / BN;
-    const int64_t bm = blockIdx.x / nbn, bn = blockIdx.x % nbn;
+    int64_t bm, bn;
+    tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, bm, bn);
     const int64_t m0 = bm * BM, n0 = bn * BN;
     const int64_t mt0 = m0 / 16, nt0 = n0 / 16;
     const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
@@ -437,7 +464,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(LinParams p) {
         else wait_vmcnt<0>();
         // every wave's share of stage kt is in LDS, and every wave has
         // finished reading the stage that the next issue overwrites
-        __syncthreads();
+        lds_barrier();
         if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
 
         const uint8_t* base = lds + (kt % S) * C::STAGE;
@@ -510,6 +537,391 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(LinParams p) {
             }
         }
         // the band is written and read back by this wave only
+        __builtin_amdgcn_wave_barrier();
+        for (int q = lane; q < 16 * chunks_per_row; q += 64) {
+            const int row = q / chunks_per_row, ch = q % chunks_per_row;
+            const int64_t m = rbase + row;
+            const int64_t n = col0 + (int64_t)ch * 16 / esz;
+            if (m < p.M && n < p.N)
+                *(u4*)((uint8_t*)p.ep.y + (m * p.ep.ldy + n) * esz) =
+                    *(const u4*)(scratch + row * C::EPI_ROW + ch * 16);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Same tiling, with the fragments of k-tile kt+1 read from LDS into a
+// second register set while the MFMAs of k-tile kt run. Every wave holds
+// k-tile kt in registers before the barrier of iteration kt, so that
+// iteration refills slot kt % S with k-tile kt + S: S = 2 already keeps one
+// k-tile of DMA in flight behind the one being read.
+template <int V, int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(LinParams p) {
+    using C = GemmCfg<V, BM, BN, WM, WN, S>;
+    using Acc = typename VT<V>::Acc;
+    constexpr int NW = C::NW, FM = C::FM, FN = C::FN, BT = C::BT;
+    constexpr int BC = VT<V>::B_CHUNKS;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int64_t bm, bn;
+    tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, bm, bn);
+    const int64_t m0 = bm * BM, n0 = bn * BN;
+    const int64_t mt0 = m0 / 16, nt0 = n0 / 16;
+    const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
+    const int KT = (int)p.KT;
+
+    const int64_t a_strips = mtiles - mt0 < BM / 16 ? mtiles - mt0 : BM / 16;
+    const int64_t b_strips = ntiles - nt0 < BN / 16 ? ntiles - nt0 : BN / 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.a + mt0 * p.KT * 2048), (short)0, (int)(a_strips * p.KT * 2048),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + nt0 * p.KT * BT), (short)0, (int)(b_strips * p.KT * BT), 0x00020000);
+
+    auto issue = [&](int kt, int stage) {
+        uint8_t* base = lds + stage * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::A_LD / NW; ++i) {
+            const int slot = wave + NW * i, sub = slot >> 1, h = slot & 1;
+            const int off = (sub * KT + kt) * 2048 + h * 1024 + lane * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + slot * 1024), 16, off, 0,
+                                                     0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_LD / NW; ++i) {
+            const int slot = wave + NW * i;
+            int off;
+            if constexpr (BT == 2048) off = ((slot >> 1) * KT + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
+            else off = (slot * KT + kt) * 1024 + lane * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + C::A_BYTES + slot * 1024),
+                                                     16, off, 0, 0, 0);
+        }
+    };
+    // Wait until this wave's loads of a k-tile are complete, given how many
+    // k-tiles it has issued after that one (at most S - 1).
+    auto wait_behind = [&](int after) {
+        if (S > 1 && after >= S - 1) wait_vmcnt<C::LDPW * (S - 1)>();
+        else if (S > 2 && after == S - 2) wait_vmcnt<C::LDPW * (S - 2)>();
+        else if (S > 3 && after == 1) wait_vmcnt<C::LDPW>();
+        else wait_vmcnt<0>();
+    };
+    struct Frag {
+        u4 a[FM][2];
+        u4 b[FN][BC];
+    };
+    auto read_frags = [&](int kt, Frag& f) {
+        const uint8_t* base = lds + (kt % S) * C::STAGE;
+        const uint8_t* abase = base + (wm * FM) * 2048 + lane * 16;
+        const uint8_t* bbase = base + C::A_BYTES + (wn * FN) * BT + lane * 16;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int c = 0; c < BC; ++c) f.b[j][c] = *(const u4*)(bbase + j * BT + c * 1024);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            f.a[i][0] = *(const u4*)(abase + i * 2048);
+            f.a[i][1] = *(const u4*)(abase + i * 2048 + 1024);
+        }
+    };
+
+    Acc acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+    auto compute = [&](const Frag& f) {
+        if constexpr (V == V_FP8) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const v8i af = as_v8i(f.a[i][0], f.a[i][1]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8(af, as_v8i(f.b[j][0], f.b[j][1]), acc[i][j]);
+            }
+        } else if constexpr (V == V_FP8X) {
+            v8h bh[FN][4];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) decode32(f.b[j][0], f.b[j][1], bh[j]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                v8h ah[4];
+                decode32(f.a[i][0], f.a[i][1], ah);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[i][j] = mfma_f16(ah[q], bh[j][q], acc[i][j]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mma_w4a8(acc[i][j], f.a[i][0], f.a[i][1], f.b[j][0]);
+        }
+    };
+
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        if (s < KT) issue(s, s);
+    // One k-step with a successor (kt + 1 < KT): fragments of kt are in
+    // `cur`, those of kt+1 are read into `nxt` while the MFMAs of kt run.
+    // The body has no branch around the LDS reads, so the MFMAs only wait
+    // for `cur`, whose reads completed before the barrier.
+    auto step = [&](int kt, Frag& cur, Frag& nxt) {
+        // k-tiles kt+2 .. min(kt+S-1, KT-1) were issued after kt+1
+        wait_behind(KT - 2 - kt < S - 2 ? KT - 2 - kt : S - 2);
+        lds_barrier();
+        if (kt + S < KT) issue(kt + S, kt % S);
+        read_frags(kt + 1, nxt);
+        compute(cur);
+    };
+    Frag f0, f1;
+    wait_behind(KT - 1 < S - 1 ? KT - 1 : S - 1);
+    lds_barrier();
+    read_frags(0, f0);
+    // unrolled by two so that the two fragment sets swap roles without copies
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);
+    }
+    if (kt + 1 < KT) {
+        step(kt, f0, f1);
+        compute(f1);
+    } else {
+        compute(f0);
+    }
+
+    // ---- epilogue (as gemm_kernel)
+    __syncthreads();
+    wait_vmcnt<0>();
+    const float sa = (V == V_FP8 || V == V_FP8X) ? *p.ep.a_scale : 1.0f;
+    const int esz = out_size(p.ep.ydt);
+    uint8_t* scratch = lds + wave * C::EPI_WAVE;
+    const int chunks_per_row = FN * 16 * esz / 16;
+    const int64_t col0 = n0 + wn * FN * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t rbase = m0 + (wm * FM + i) * 16;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int c = j * 16 + (lane & 15);
+            const int64_t n = col0 + c;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * (lane >> 4) + r;
+                const uint32_t bits = (n < p.N && rbase + row < p.M)
+                                          ? out_bits<V>(p.ep, sa, rbase + row, n, acc[i][j][r])
+                                          : 0u;
+                uint8_t* d = scratch + row * C::EPI_ROW + c * esz;
+                if (esz == 4) *(uint32_t*)d = bits;
+                else if (esz == 2) *(uint16_t*)d = (uint16_t)bits;
+                else *d = (uint8_t)bits;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (int q = lane; q < 16 * chunks_per_row; q += 64) {
+            const int row = q / chunks_per_row, ch = q % chunks_per_row;
+            const int64_t m = rbase + row;
+            const int64_t n = col0 + (int64_t)ch * 16 / esz;
+            if (m < p.M && n < p.N)
+                *(u4*)((uint8_t*)p.ep.y + (m * p.ep.ldy + n) * esz) =
+                    *(const u4*)(scratch + row * C::EPI_ROW + ch * 16);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Exact fp8 tile kernel with the k range split between two groups of
+// waves. Every 16x128 operand tile holds, per lane, two 16-byte halves that
+// feed two f16 MFMAs each; wave group g reads and decodes only half g of
+// each tile, so a wave with a 64x64 output tile decodes two fp8 pairs per
+// MFMA instead of four and reads half the LDS bytes. The two groups' fp32
+// partial sums are added through LDS at the end (each group finishes half of
+// the rows; a + b == b + a, so the result does not depend on which group).
+template <int BM, int BN, int WM, int WN, int S>
+struct KsCfg {
+    static constexpr int SW = WM * WN, NW = 2 * SW;
+    static constexpr int A_BYTES = (BM / 16) * 2048, B_BYTES = (BN / 16) * 2048;
+    static constexpr int STAGE = A_BYTES + B_BYTES, RING = S * STAGE;
+    static constexpr int FM = BM / (16 * WM), FN = BN / (16 * WN);
+    static constexpr int A_LD = A_BYTES / 1024, B_LD = B_BYTES / 1024;
+    static constexpr int LDPW = (A_LD + B_LD) / NW;
+    static constexpr int XCH = (FM / 2) * FN * 4 * 64 * 4;  // bytes a wave hands to its partner
+    static constexpr int EPI_ROW = FN * 16 * 4 + 16, EPI_WAVE = 16 * EPI_ROW;
+    static constexpr int LDS0 = RING > NW * XCH ? RING : NW * XCH;
+    static constexpr int LDS = LDS0 > NW * EPI_WAVE ? LDS0 : NW * EPI_WAVE;
+    static_assert(A_LD % NW == 0 && B_LD % NW == 0, "stage loads must split evenly over waves");
+    static_assert(FM % 2 == 0, "each group finishes half of a wave's row tiles");
+    static_assert(LDPW * (S - 1) < 64, "vmcnt range");
+};
+
+template <int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
+    using C = KsCfg<BM, BN, WM, WN, S>;
+    constexpr int NW = C::NW, SW = C::SW, FM = C::FM, FN = C::FN;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = wave / SW, sw = wave % SW, wm = sw / WN, wn = sw % WN;
+    int64_t bm, bn;
+    tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, bm, bn);
+    const int64_t m0 = bm * BM, n0 = bn * BN;
+    const int64_t mt0 = m0 / 16, nt0 = n0 / 16;
+    const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
+    const int KT = (int)p.KT;
+
+    const int64_t a_strips = mtiles - mt0 < BM / 16 ? mtiles - mt0 : BM / 16;
+    const int64_t b_strips = ntiles - nt0 < BN / 16 ? ntiles - nt0 : BN / 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.a + mt0 * p.KT * 2048), (short)0, (int)(a_strips * p.KT * 2048),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + nt0 * p.KT * 2048), (short)0, (int)(b_strips * p.KT * 2048), 0x00020000);
+
+    auto issue = [&](int kt, int stage) {
+        uint8_t* base = lds + stage * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::A_LD / NW; ++i) {
+            const int slot = wave + NW * i;
+            const int off = ((slot >> 1) * KT + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + slot * 1024), 16, off, 0,
+                                                     0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_LD / NW; ++i) {
+            const int slot = wave + NW * i;
+            const int off = ((slot >> 1) * KT + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + C::A_BYTES + slot * 1024),
+                                                     16, off, 0, 0, 0);
+        }
+    };
+    auto wait_behind = [&](int after) {
+        if (S > 1 && after >= S - 1) wait_vmcnt<C::LDPW * (S - 1)>();
+        else if (S > 2 && after == S - 2) wait_vmcnt<C::LDPW * (S - 2)>();
+        else if (S > 3 && after == 1) wait_vmcnt<C::LDPW>();
+        else wait_vmcnt<0>();
+    };
+    struct Frag {
+        u4 a[FM];
+        u4 b[FN];
+    };
+    auto read_frags = [&](int kt, Frag& f) {
+        const uint8_t* base = lds + (kt % S) * C::STAGE + g * 1024 + lane * 16;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) f.b[j] = *(const u4*)(base + C::A_BYTES + (wn * FN + j) * 2048);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) f.a[i] = *(const u4*)(base + (wm * FM + i) * 2048);
+    };
+
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+
+    auto compute = [&](const Frag& f) {
+        v8h bh[FN][2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            bh[j][0] = e4m3x8_to_f16(f.b[j][0], f.b[j][1]);
+            bh[j][1] = e4m3x8_to_f16(f.b[j][2], f.b[j][3]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const v8h a0 = e4m3x8_to_f16(f.a[i][0], f.a[i][1]);
+            const v8h a1 = e4m3x8_to_f16(f.a[i][2], f.a[i][3]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j] = mfma_f16(a0, bh[j][0], acc[i][j]);
+                acc[i][j] = mfma_f16(a1, bh[j][1], acc[i][j]);
+            }
+        }
+    };
+    auto step = [&](int kt, Frag& cur, Frag& nxt) {
+        wait_behind(KT - 2 - kt < S - 2 ? KT - 2 - kt : S - 2);
+        lds_barrier();
+        if (kt + S < KT) issue(kt + S, kt % S);
+        read_frags(kt + 1, nxt);
+        compute(cur);
+    };
+
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        if (s < KT) issue(s, s);
+    Frag f0, f1;
+    wait_behind(KT - 1 < S - 1 ? KT - 1 : S - 1);
+    lds_barrier();
+    read_frags(0, f0);
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);
+    }
+    if (kt + 1 < KT) {
+        step(kt, f0, f1);
+        compute(f1);
+    } else {
+        compute(f0);
+    }
+
+    // ---- add the two groups' partial sums: group 0 finishes row tiles
+    // [0, FM/2) of its wave tile, group 1 row tiles [FM/2, FM)
+    wait_vmcnt<0>();
+    __syncthreads();
+    const bool low = g == 0;
+    {
+        float* out = (float*)(lds + wave * C::XCH);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            if ((i < FM / 2) != low)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        out[(((i % (FM / 2)) * FN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    {
+        const float* in = (const float*)(lds + ((1 - g) * SW + sw) * C::XCH);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            if ((i < FM / 2) == low)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][j][r] += in[(((i % (FM / 2)) * FN + j) * 4 + r) * 64 + lane];
+    }
+    __syncthreads();
+
+    // ---- epilogue: per 16-row band, values staged in LDS, 16-byte stores
+    const float sa = *p.ep.a_scale;
+    const int esz = out_size(p.ep.ydt);
+    uint8_t* scratch = lds + wave * C::EPI_WAVE;
+    const int chunks_per_row = FN * 16 * esz / 16;
+    const int64_t col0 = n0 + wn * FN * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        if ((i < FM / 2) != low) continue;
+        const int64_t rbase = m0 + (wm * FM + i) * 16;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int c = j * 16 + (lane & 15);
+            const int64_t n = col0 + c;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * (lane >> 4) + r;
+                const uint32_t bits = (n < p.N && rbase + row < p.M)
+                                          ? out_bits<V_FP8X>(p.ep, sa, rbase + row, n, acc[i][j][r])
+                                          : 0u;
+                uint8_t* d = scratch + row * C::EPI_ROW + c * esz;
+                if (esz == 4) *(uint32_t*)d = bits;
+                else if (esz == 2) *(uint16_t*)d = (uint16_t)bits;
+                else *d = (uint8_t)bits;
+            }
+        }
         __builtin_amdgcn_wave_barrier();
         for (int q = lane; q < 16 * chunks_per_row; q += 64) {
             const int row = q / chunks_per_row, ch = q % chunks_per_row;
@@ -607,9 +1019,66 @@ static hipError_t launch_gemm(const LinParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int V, int BM, int BN, int WM, int WN, int S>
+static hipError_t launch_gemm_pipe(const LinParams& p, hipStream_t stream) {
+    using C = GemmCfg<V, BM, BN, WM, WN, S>;
+    static std::atomic<uint64_t> configured{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (!(configured.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute((const void*)gemm_pipe_kernel<V, BM, BN, WM, WN, S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (e != hipSuccess) return e;
+        configured.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    const int64_t blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    gemm_pipe_kernel<V, BM, BN, WM, WN, S><<<(unsigned)blocks, 64 * WM * WN, C::LDS, stream>>>(p);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+static hipError_t launch_gemm_ks(const LinParams& p, hipStream_t stream) {
+    using C = KsCfg<BM, BN, WM, WN, S>;
+    static std::atomic<uint64_t> configured{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (!(configured.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute((const void*)gemm_ks_kernel<BM, BN, WM, WN, S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (e != hipSuccess) return e;
+        configured.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    const int64_t blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    gemm_ks_kernel<BM, BN, WM, WN, S><<<(unsigned)blocks, 128 * WM * WN, C::LDS, stream>>>(p);
+    return hipGetLastError();
+}
+
+
+
+// Kernel choice for the tiled path, from measured M=1024 sweeps on the
+// Llama-3-8B projection shapes. "One tile per CU" shapes (at most 256
+// 128x128 tiles) favour kernels that hide latency inside one block: the
+// k-split exact kernel and the register-prefetching fp8 kernel with a
+// three-stage ring; shapes with many 256x256 tiles favour the big fp8 tile.
+constexpr int64_t CUS = 256;
 template <int V>
 static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
-    return launch_gemm<V, 128, 128, 2, 2, 2>(p, stream);
+    const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if constexpr (V == V_FP8X) {
+        if (t128 <= CUS) return launch_gemm_ks<128, 128, 2, 2, 2>(p, stream);
+        return launch_gemm<V, 128, 128, 2, 2, 2>(p, stream);
+    } else if constexpr (V == V_FP8) {
+        if (t128 <= CUS) return launch_gemm_pipe<V, 128, 128, 4, 2, 3>(p, stream);
+        if (t256 >= 3 * CUS / 2) return launch_gemm<V, 256, 256, 4, 4, 2>(p, stream);
+        return launch_gemm<V, 128, 128, 2, 4, 2>(p, stream);
+    } else {
+        return launch_gemm<V, 128, 128, 2, 2, 2>(p, stream);
+    }
 }
 
 hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipStream_t stream) {
