@@ -56,22 +56,43 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// x / s for the dynamic per-tensor quantizers, from y = 1/s (computed once
+// with an IEEE division) and one fma residual correction:
+// q = x*y, r = x - q*s (exact), q' = q + r*y, sign taken from x (s > 0).
+// For every scale s = amax/448 with amax a finite bf16 or f16 value and
+// 2^-90 <= s <= 2^90, and every x of the same format with |x| <= amax, this
+// is the IEEE quotient x/s bit for bit wherever |x/s| >= 2^-10; below that
+// (tiny x, whose residual may underflow) both quotients stay below 2^-10
+// with the sign of x, so both encode to the same signed zero (checked by
+// enumerating all such pairs).
+// Callers use the IEEE division for scales outside that range.
+__device__ __forceinline__ bool recip_div_ok(float s) { return s >= 0x1p-90f && s <= 0x1p90f; }
+__device__ __forceinline__ float div_by_scale(float x, float s, float y) {
+    const float q = x * y;
+    const float r = __builtin_fmaf(-q, s, x);
+    return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+}
+
 // fp32 -> OCP E4M3 code: round to nearest even on the bit pattern,
 // saturate magnitudes >= 448 to 0x7E, keep the sign (so -0 -> 0x80).
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    uint32_t u = __float_as_uint(v);
-    uint32_t s = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return s | 0x7Fu;  // NaN
-    if (a >= 0x43E00000u) return s | 0x7Eu; // |v| >= 448
-    if (a < 0x3C800000u) {                  // |v| < 2^-6: subnormal grid of 2^-9
-        float t = __uint_as_float(a) * 512.0f;  // exact scaling
-        return s | (uint32_t)__builtin_rintf(t);
-    }
+    // Branch-free (both candidates computed, then selected): the quantizers
+    // encode 16-32 values per lane, and data-dependent branches diverge.
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t s = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    // |v| < 2^-6: subnormal grid of 2^-9, exact scaling then ties-to-even;
+    // the input is clamped so the conversion stays in range (t <= 8)
+    const float t = __uint_as_float(a < 0x3C800000u ? a : 0x3C800000u) * 512.0f;
+    const uint32_t sub = (uint32_t)__builtin_rintf(t);
     // normal: keep 3 of 23 mantissa bits with ties to even, carry into the
     // exponent, then rebias the exponent from 127 to 7 (120 << 3 = 960)
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return s | ((r >> 20) - 960u);
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    const uint32_t nrm = (r >> 20) - 960u;
+    uint32_t c = a < 0x3C800000u ? sub : nrm;
+    c = a >= 0x43E00000u ? 0x7Eu : c;  // |v| >= 448 (and inf) saturate
+    c = a > 0x7F800000u ? 0x7Fu : c;   // NaN
+    return s | c;
 }
 
 // ------------------------------------------------------------- reductions

@@ -16,18 +16,20 @@
 namespace bql {
 
 constexpr int QT = 256;          // threads per block
-constexpr int MAX_PARTIALS = 256;
+constexpr int MAX_PARTIALS = 1024;  // fills the 4 KiB partials region of the workspace
+constexpr int AMAX_LOADS = 8;       // 16-byte loads in flight per thread
 
 int amax_blocks(int64_t numel) {
     int64_t vecs = (numel + 7) / 8;
-    int64_t b = (vecs + QT * 4 - 1) / (QT * 4);
+    int64_t b = (vecs + QT * AMAX_LOADS - 1) / (QT * AMAX_LOADS);
     if (b < 1) b = 1;
     if (b > MAX_PARTIALS) b = MAX_PARTIALS;
     return (int)b;
 }
 
 // Each block: max of |x| (as ordered magnitude bits) over a grid-stride
-// share of 8-element vectors; block 0 also takes the ragged tail.
+// range of 16-byte vectors, AMAX_LOADS loads in flight per thread; the
+// scalar tail (numel % 8) goes to block 0.
 __global__ __launch_bounds__(QT) void amax_partial_kernel(const uint16_t* __restrict__ x,
                                                           int64_t numel,
                                                           uint32_t* __restrict__ partial) {
@@ -37,28 +39,22 @@ __global__ __launch_bounds__(QT) void amax_partial_kernel(const uint16_t* __rest
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * QT;
     int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x;
-    for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight per thread
-        u4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&xv[i + u * stride]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t lo = mag16(v[u][j] & 0xFFFFu), hi = mag16(v[u][j] >> 16);
-                m = m > lo ? m : lo;
-                m = m > hi ? m : hi;
-            }
-    }
-    for (; i < nvec; i += stride) {
-        u4 v = __builtin_nontemporal_load(&xv[i]);
+    auto fold = [&](const u4& v) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t lo = mag16(v[j] & 0xFFFFu), hi = mag16(v[j] >> 16);
+            const uint32_t lo = mag16(v[j] & 0xFFFFu), hi = mag16(v[j] >> 16);
             m = m > lo ? m : lo;
             m = m > hi ? m : hi;
         }
+    };
+    for (; i + (AMAX_LOADS - 1) * stride < nvec; i += AMAX_LOADS * stride) {
+        u4 v[AMAX_LOADS];
+#pragma unroll
+        for (int u = 0; u < AMAX_LOADS; ++u) v[u] = __builtin_nontemporal_load(&xv[i + u * stride]);
+#pragma unroll
+        for (int u = 0; u < AMAX_LOADS; ++u) fold(v[u]);
     }
+    for (; i < nvec; i += stride) fold(__builtin_nontemporal_load(&xv[i]));
     if (blockIdx.x == 0) {
         int64_t t = nvec * 8 + threadIdx.x;
         if (t < numel) {
@@ -108,22 +104,31 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
     const int64_t nvec = numel / 8;
     const u4* xv = (const u4*)x;
     u2* qv = (u2*)xq;
-    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
-         i += (int64_t)gridDim.x * QT) {
-        u4 v = __builtin_nontemporal_load(&xv[i]);
-        uint32_t c[8];
+    auto body = [&](auto div) {
+        for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
+             i += (int64_t)gridDim.x * QT) {
+            u4 v = __builtin_nontemporal_load(&xv[i]);
+            uint32_t c[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            c[2 * j] = e4m3_encode(to_f32<DT>(v[j] & 0xFFFFu) / s);
-            c[2 * j + 1] = e4m3_encode(to_f32<DT>(v[j] >> 16) / s);
+            for (int j = 0; j < 4; ++j) {
+                c[2 * j] = e4m3_encode(div(to_f32<DT>(v[j] & 0xFFFFu)));
+                c[2 * j + 1] = e4m3_encode(div(to_f32<DT>(v[j] >> 16)));
+            }
+            u2 o = {pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+            __builtin_nontemporal_store(o, &qv[i]);
         }
-        u2 o = {pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
-        __builtin_nontemporal_store(o, &qv[i]);
-    }
-    if (blockIdx.x == 0) {
-        int64_t t = nvec * 8 + threadIdx.x;
-        if (t < numel) xq[t] = (uint8_t)e4m3_encode(to_f32<DT>(x[t]) / s);
-    }
+        if (blockIdx.x == 0) {
+            int64_t t = nvec * 8 + threadIdx.x;
+            if (t < numel) xq[t] = (uint8_t)e4m3_encode(div(to_f32<DT>(x[t])));
+        }
+    };
+    // a given (static) scale is any float: only the dynamic scale amax/448
+    // takes the reciprocal form
+    const float y = 1.0f / s;
+    if (SCALE_FROM == 0 && recip_div_ok(s))
+        body([&](float v) { return div_by_scale(v, s, y); });
+    else
+        body([&](float v) { return v / s; });
 }
 
 // ------------------------------------------------ packed 8-bit activations
@@ -140,8 +145,49 @@ __device__ __forceinline__ int64_t packed_offset(int64_t m, int64_t k, int64_t K
            ((m & 15) + 16 * ((k >> 5) & 3)) * 16 + (k & 15);
 }
 
-// Grid-stride over items of 8 consecutive k of one row (KT*16 items per
-// row, the padding up to the tile edge included).
+// the tile loop of cast_e4m3_packed_kernel, for a given x -> x/s
+template <int DT, class Div>
+__device__ __forceinline__ void cast_packed_tiles(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                  int64_t KT, uint8_t* __restrict__ xq, int64_t tiles,
+                                                  int lane, int r, int g, Div div) {
+    constexpr int WPB = QT / 64;
+    for (int64_t t = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6); t < tiles;
+         t += (int64_t)gridDim.x * WPB) {
+        const int64_t mt = t / KT, kt = t % KT;
+        const int64_t m = mt * 16 + r, k = kt * 128 + 32 * g;
+        u4 out[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t c[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) c[j] = 0;
+            if (m < M && k + 16 * h < K) {
+                const u4* src = (const u4*)(x + m * K + k + 16 * h);
+                const u4 v0 = __builtin_nontemporal_load(src), v1 = __builtin_nontemporal_load(src + 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    c[2 * j] = e4m3_encode(div(to_f32<DT>(v0[j] & 0xFFFFu)));
+                    c[2 * j + 1] = e4m3_encode(div(to_f32<DT>(v0[j] >> 16)));
+                    c[8 + 2 * j] = e4m3_encode(div(to_f32<DT>(v1[j] & 0xFFFFu)));
+                    c[8 + 2 * j + 1] = e4m3_encode(div(to_f32<DT>(v1[j] >> 16)));
+                }
+            }
+            out[h] = u4{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
+                        pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15])};
+        }
+        uint8_t* tile = xq + t * 2048 + lane * 16;
+        *(u4*)tile = out[0];
+        *(u4*)(tile + 1024) = out[1];
+    }
+}
+
+// One wave per 16 x 128 packed tile (row tile mt, k-tile kt), grid-stride
+// over tiles. Lane l = r + 16 g holds row 16 mt + r, k = 128 kt + 32 g ..
+// +31: it reads those 32 inputs (64 contiguous bytes; a row's four lanes read
+// 256 contiguous bytes) and writes the 16 codes of k .. k+15 at tile + 16 l
+// and those of k+16 .. k+31 at tile + 1024 + 16 l, so each wave stores two
+// contiguous 1 KiB runs. Rows past M and k past K (K is a multiple of 16)
+// are written as zero codes.
 template <int DT>
 __global__ __launch_bounds__(QT) void cast_e4m3_packed_kernel(const uint16_t* __restrict__ x,
                                                               int64_t M, int64_t K, int64_t KT,
@@ -155,21 +201,14 @@ __global__ __launch_bounds__(QT) void cast_e4m3_packed_kernel(const uint16_t* __
         if (scale_out) *scale_out = s;
         if (scale_ws) *scale_ws = s;
     }
-    const int64_t per_row = KT * 16, total = M * per_row;
-    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < total; i += (int64_t)gridDim.x * QT) {
-        const int64_t m = i / per_row, k = (i % per_row) * 8;
-        uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (k < K) {  // K is a multiple of 16: the 8 values are all inside or all padding
-            const u4 v = __builtin_nontemporal_load((const u4*)(x + m * K + k));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[2 * j] = e4m3_encode(to_f32<DT>(v[j] & 0xFFFFu) / s);
-                c[2 * j + 1] = e4m3_encode(to_f32<DT>(v[j] >> 16) / s);
-            }
-        }
-        *(u2*)(xq + packed_offset(m, k, KT)) =
-            u2{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
-    }
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int64_t tiles = ((M + 15) / 16) * KT;
+    const float y = 1.0f / s;
+    if (recip_div_ok(s))
+        cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g,
+                              [&](float v) { return div_by_scale(v, s, y); });
+    else
+        cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, [&](float v) { return v / s; });
 }
 
 // Row-major 8-bit codes [M, K] -> packed layout; grid-stride over 16-byte
@@ -197,7 +236,7 @@ hipError_t launch_quant_dynamic_packed(const void* x, int xdt, int64_t M, int64_
     const int nb = amax_blocks(numel);
     amax_partial_kernel<<<nb, QT, 0, stream>>>((const uint16_t*)x, numel, partial);
     const int64_t KT = (K + 127) / 128;
-    int64_t blocks = (M * KT * 16 + QT - 1) / QT;
+    int64_t blocks = (((M + 15) / 16) * KT + QT / 64 - 1) / (QT / 64);
     if (blocks > 8192) blocks = 8192;
     if (xdt == IN_BF16)
         cast_e4m3_packed_kernel<IN_BF16><<<(unsigned)blocks, QT, 0, stream>>>(
