@@ -20,6 +20,8 @@ Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -42,8 +44,96 @@ SHAPES = wl.CFG3_SHAPES
 ROTATE_BYTES = 640 * 2 ** 20  # > 2 x 256 MiB Infinity Cache
 
 
+CALIBRATION_COPY_BYTES = 256 * 2 ** 20
+# sources the tiled GEMM kernels are built from; a traffic summary is only
+# used while they are unchanged
+KERNEL_SOURCES = ["bit_quantized_linear_amd/csrc/linear.hip",
+                  "bit_quantized_linear_amd/csrc/device.h",
+                  "bit_quantized_linear_amd/csrc/kernels.h"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_m1024_n28672_k4096_hbm_traffic.txt")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(key):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            fields = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != kernel_source_hash():
+        return None
+    v = fields.get(key)
+    return int(v.strip()) if v else None
+
+
+def summarize_traffic(fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs of `bench.py --roofline-only` (FETCH_SIZE,
+    then WRITE_SIZE) into HBM bytes per launch of the two dominant GEMMs.
+    Each counter is scaled by what it reads for the run's last plain device
+    copy (CALIBRATION_COPY_BYTES read and written)."""
+    def per_dispatch(d, counter):
+        rows = []
+        for root, _, files in os.walk(d):
+            for f in files:
+                if f.endswith("counter_collection.csv"):
+                    with open(os.path.join(root, f)) as fh:
+                        rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        acc = {}
+        for r in rows:
+            k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
+        return sorted(acc.items())
+    out = {}
+    lines = []
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        disp = per_dispatch(d, counter)
+        copies = [v for (i, name), v in disp if "copyBuffer" in name]
+        if not copies:
+            raise SystemExit(f"no calibration copy among the {counter} dispatches in {d}")
+        factor = copies[-1] / CALIBRATION_COPY_BYTES
+        lines.append(f"  {counter}: calibration copy of {CALIBRATION_COPY_BYTES} B reads {copies[-1]:.1f}"
+                     f" counter units -> {1.0 / factor:.2f} B per unit")
+        for tag, sig in (("exact", "gemm_kernel<3,"), ("fast", "gemm_kernel<0,")):
+            vals = [v for (i, name), v in disp if sig in name.replace(" ", "")]
+            if not vals:
+                raise SystemExit(f"no {sig} dispatches in {d}")
+            b = sum(vals) / len(vals) / factor
+            out.setdefault(tag, 0.0)
+            out[tag] += b
+            lines.append(f"  {tag} GEMM {counter}: {len(vals)} dispatches, {b / 1e6:.1f} MB per launch")
+    alg = algorithmic_bytes_gemm(1024, 28672, 4096)
+    text = ["# HBM traffic of the dominant GEMM launches, M=1024 N=28672 K=4096",
+            "# (tiled GEMM, exact = f16 MFMA on decoded fp8, fast = fp8 MFMA; pre-quantized A)",
+            "commands (repo root; cd /tmp && export TMPDIR=/tmp first, then back):",
+            "  rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --roofline-only",
+            "  rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python3 bench.py --roofline-only",
+            "  python3 bench.py --summarize-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+            f"source_sha256: {kernel_source_hash()}",
+            "details:"] + lines + [
+            f"  algorithmic bytes per launch (Aq + Wq + bf16 Y + scales): {alg}",
+            f"exact_hbm_bytes_per_launch: {int(round(out['exact']))}",
+            f"fast_hbm_bytes_per_launch: {int(round(out['fast']))}"]
+    with open(TRAFFIC_SUMMARY, "w") as fh:
+        fh.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
+def algorithmic_bytes_gemm(M, N, K):
+    """The GEMM alone: fp8 A and W, bf16 Y, two scales."""
+    return M * K + N * K + 2 * M * N + 8
 
 
 def algorithmic_bytes(M, N, K):
@@ -159,7 +249,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel launches (for a rocprofv3 run of that kernel)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc output folders")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -223,14 +318,23 @@ def main():
         peak = PEAK_FP8_TFLOPS if fast else PEAK_F16_TFLOPS
         ach = fl / us / 1e6
         return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None,
-                "kernel": f"gemm_kernel<{'V_FP8' if fast else 'V_FP8X'}> M={M} N={N} K={K}",
+                "frac": round(ach / peak, 4),
+                "traffic": read_traffic("fast_hbm_bytes_per_launch" if fast else "exact_hbm_bytes_per_launch"),
+                "algorithmic_bytes_per_launch": algorithmic_bytes_gemm(M, N, K),
+                "kernel": (f"gemm_kernel<V_FP8,256,256,4,4,2> M={M} N={N} K={K}" if fast else
+                           f"gemm_kernel<V_FP8X,128,128,2,2,2> M={M} N={N} K={K}"),
                 "avg_launch_us": round(us, 2), "flops_per_launch": fl}
     log("kernel rooflines ...")
     roof = kernel_roofline(False)
     roof_fast = kernel_roofline(True)
     if args.roofline_only:
-        print(json.dumps({"roofline": roof, "fast_accum_roofline": roof_fast}), flush=True)
+        # plain device copy of known size: the calibration for HBM byte counters
+        src = torch.empty(CALIBRATION_COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"roofline": roof, "fast_accum_roofline": roof_fast,
+                          "calibration_copy_bytes": CALIBRATION_COPY_BYTES}), flush=True)
         return
 
     # fast accumulation (fp8 matrix cores' own accumulation), same step
