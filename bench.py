@@ -40,6 +40,7 @@ METRIC = "fp8 linear TFLOP/s at M=1024 + HBM GB/s at M=1, Llama-shaped N×K"
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_F16_TFLOPS = 2500.0
+PEAK_I8_TOPS = 5000.0
 SHAPES = wl.CFG3_SHAPES
 ROTATE_BYTES = 640 * 2 ** 20  # > 2 x 256 MiB Infinity Cache
 
@@ -240,6 +241,98 @@ def cpu_baseline(host_w, act_bits, M, rows_per_shape):
                       f"computed ({t_quant + t_dot:.1f} s), dot-product time scaled to {M} rows"}
 
 
+def f16_bits_to_f32(bits):
+    return bits.view(np.float16).astype(np.float32)
+
+
+def rotation(pw, bql, nbytes):
+    """Device copies of a packed weight, enough that a pass over them moves
+    more than ROTATE_BYTES."""
+    n = max(2, -(-ROTATE_BYTES // nbytes))
+    return [bql.PackedWeight(pw.packed.clone(), pw.scales.clone(), pw.N, pw.K, pw.fmt) for _ in range(n)]
+
+
+def timed_graphs(step, nslots, steps, warmup):
+    graphs = capture_graphs(step, nslots)
+    return time_steps(lambda i: graphs[i % nslots].replay(), steps, warmup)
+
+
+def bench_w8a16(bql, dev, steps, warmup):
+    """Weight-only fp8 decode GEMV: M in {1, 8}, K = N = 4096, E4M3 weight
+    with per-channel fp16 scales, fp16 activations and output."""
+    N = K = 4096
+    g = wl.rng(2, 0)
+    bits = wl.weight(g, N, K, "f16")
+    sbits = wl.w8a16_channel_scales(g, f16_bits_to_f32(bits))
+    w = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+    sc = torch.from_numpy(sbits.view(np.int16)).to(dev).view(torch.float16)
+    rot = rotation(bql.prepack_weight(w, "fp8_channel", scales=sc), bql, N * K)
+    out = {"workload": "W8A16 decode GEMV, K=N=4096, E4M3 weight with per-channel fp16 scales "
+                       "u*amax_n/448 (u ~ U[0.5,2]), fp16 A N(0,1) and fp16 out",
+           "weight_rotation_copies": len(rot)}
+    for M in (1, 8):
+        a = torch.from_numpy(wl.activation(wl.rng(2, M, 3), M, K, "f16").view(np.int16)).to(dev).view(torch.float16)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = torch.empty(max(256, bql.lib().bql_w8a16_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=dev)
+        sec = timed_graphs(lambda i: bql.w8a16_linear(a, rot[i % len(rot)], out=y, ws=ws), len(rot), steps, warmup)
+        byts = N * K + 2 * N + 2 * M * K + 2 * M * N
+        gbs = byts / sec / 1e9
+        out[f"M{M}"] = {"value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(sec * 1e6, 2),
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return out
+
+
+def bench_w4a8(bql, dev, steps, warmup):
+    """W4A8 per-channel integer linear over K = N in {4096, 5120, 6656, 8192}:
+    int8 per-token activations (quantized before the timed region), int4
+    weights with fp16 channel scales, int32 accumulation, fp16 out.  One step
+    runs the four linears."""
+    shapes = wl.CFG5_KN
+    rots = []
+    for idx, n in enumerate(shapes):
+        g = wl.rng(5, idx, 1)
+        w4 = wl.int4_weight(g, n, n)
+        sbits = wl.w4a8_channel_scales(g, n)
+        wpk = torch.from_numpy(wl.pack_int4(w4).reshape(n, n // 2)).to(dev)
+        sc = torch.from_numpy(sbits.view(np.int16)).to(dev).view(torch.float16)
+        rots.append(rotation(bql.prepack_weight(wpk, "int4_channel", scales=sc), bql, n * n // 2))
+    nslots = max(len(r) for r in rots)
+    out = {"workload": "W4A8 per-channel integer linears K=N in {4096,5120,6656,8192}: int4 weights "
+                       "U{-8..7} with fp16 channel scales U[0.5,2]*2^-8, int8 per-token activations "
+                       "from fp16 N(0,1), int32 accumulation, fp16 out",
+           "weight_rotation_copies": [len(r) for r in rots]}
+    for M in (1024, 1):
+        aqs, sas, ys, wss = [], [], [], []
+        for idx, n in enumerate(shapes):
+            a = torch.from_numpy(wl.activation(wl.rng(5, idx, M, 3), M, n, "f16").view(np.int16)).to(dev)
+            aq, sa = bql.int8_quantize_per_token(a.view(torch.float16))
+            aqs.append(aq)
+            sas.append(sa)
+            ys.append(torch.empty((M, n), dtype=torch.float16, device=dev))
+            wss.append(torch.empty(max(256, bql.lib().bql_w4a8_linear_workspace_size(M, n, n)),
+                                   dtype=torch.uint8, device=dev))
+
+        def step(i):
+            for j in range(len(shapes)):
+                r = rots[j]
+                bql.w4a8_linear(aqs[j], sas[j], r[i % len(r)], out=ys[j], ws=wss[j])
+        sec = timed_graphs(step, nslots, steps, warmup)
+        ops = sum(2 * M * n * n for n in shapes)
+        byts = sum(n * n // 2 + M * n + 4 * M + 2 * n + 2 * M * n for n in shapes)
+        if M == 1:
+            gbs = byts / sec / 1e9
+            out["M1"] = {"value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(sec * 1e6, 2),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+        else:
+            tops = ops / sec / 1e12
+            out[f"M{M}"] = {"value": round(tops, 1), "unit": "TOP/s", "us_per_step": round(sec * 1e6, 2),
+                            "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_I8_TOPS,
+                                         "unit": "TOP/s", "frac": round(tops / PEAK_I8_TOPS, 4)}}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +439,11 @@ def main():
     _, _, _, _, (sec1, sec1_eager), flops1, byts1 = run_pass(1)
     _, _, _, _, (sec1p, _), _, _ = run_pass(1, prequant=True)
 
+    log("timing W8A16 decode ...")
+    w8a16 = bench_w8a16(bql, dev, args.steps, args.warmup)
+    log("timing W4A8 ...")
+    w4a8 = bench_w4a8(bql, dev, args.steps, args.warmup)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -383,6 +481,8 @@ def main():
             "ms_per_step": round(sec_f * 1e3, 4), "roofline": roof_fast,
         },
         "roofline": roof,
+        "w8a16": w8a16,
+        "w4a8": w4a8,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
