@@ -220,16 +220,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
         __shared__ uint32_t sh[16];
         const uint16_t* x = (const uint16_t*)p.a;
         const int64_t nvec = p.M * p.K / 8;  // K is a multiple of 16
+        constexpr int T = 64 * WAVES, HOLD = 4;
         uint32_t mb = 0;
-        for (int64_t i = threadIdx.x; i < nvec; i += 64 * WAVES) {
-            const u4 v = ((const u4*)x)[i];
+        auto fold = [&](const u4& v) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t lo = mag16(v[j] & 0xFFFFu), hi = mag16(v[j] >> 16);
                 mb = mb > lo ? mb : lo;
                 mb = mb > hi ? mb : hi;
             }
+        };
+        // With one K split the block's slice is all of A: the first HOLD*T
+        // vectors are loaded once and kept for the cast.
+        const bool whole = p.splits == 1;
+        u4 held[HOLD];
+#pragma unroll
+        for (int h = 0; h < HOLD; ++h) {
+            const int64_t i = threadIdx.x + (int64_t)h * T;
+            held[h] = whole && i < nvec ? ((const u4*)x)[i] : u4{0, 0, 0, 0};
         }
+#pragma unroll
+        for (int h = 0; h < HOLD; ++h) fold(held[h]);
+        for (int64_t i = threadIdx.x + (whole ? (int64_t)HOLD * T : 0); i < nvec; i += T) fold(((const u4*)x)[i]);
         mb = block_max_u32(mb, sh);
         const float amax = p.xdt == IN_BF16 ? to_f32<IN_BF16>(mb) : to_f32<IN_F16>(mb);
         sa = amax == 0.0f ? 1.0f : amax / 448.0f;  // IEEE division, as the standalone quantizer
@@ -237,22 +249,38 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
             if (p.scale_out) *p.scale_out = sa;
             if (p.scale_ws) *p.scale_ws = sa;
         }
-        const int64_t slice = p.kt_per_split * TILE_K, k_lo = kt_begin * TILE_K;
-        const int64_t items = p.M * slice / 8;
-        for (int64_t i = threadIdx.x; i < items; i += 64 * WAVES) {
-            const int64_t m = i / (slice / 8), kk = (i % (slice / 8)) * 8, k = k_lo + kk;
-            uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (k < p.K) {
-                const u4 v = *(const u4*)(x + m * p.K + k);
+        auto codes8 = [&](const u4& v) {
+            uint32_t c[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = v[j] & 0xFFFFu, hi = v[j] >> 16;
-                    c[2 * j] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)) / sa);
-                    c[2 * j + 1] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)) / sa);
-                }
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = v[j] & 0xFFFFu, hi = v[j] >> 16;
+                c[2 * j] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)) / sa);
+                c[2 * j + 1] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)) / sa);
             }
-            *(u2*)(aq_lds + m * slice + kk) = u2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                                                 c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+            return u2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+        };
+        const int64_t slice = p.kt_per_split * TILE_K, k_lo = kt_begin * TILE_K;
+        if (whole) {
+            // slice = [0, KT*128): cast the K real columns, zero the padding
+            const int64_t vpr = p.K / 8;  // vectors per row
+#pragma unroll
+            for (int h = 0; h < HOLD; ++h) {
+                const int64_t i = threadIdx.x + (int64_t)h * T;
+                if (i < nvec) *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(held[h]);
+            }
+            for (int64_t i = threadIdx.x + (int64_t)HOLD * T; i < nvec; i += T)
+                *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(((const u4*)x)[i]);
+            const int64_t pad = (slice - p.K) / 8;  // zero 8-byte items past K in each row
+            for (int64_t i = threadIdx.x; i < p.M * pad; i += T)
+                *(u2*)(aq_lds + (i / pad) * slice + p.K + (i % pad) * 8) = u2{0, 0};
+        } else {
+            const int64_t items = p.M * slice / 8;
+            for (int64_t i = threadIdx.x; i < items; i += T) {
+                const int64_t m = i / (slice / 8), kk = (i % (slice / 8)) * 8, k = k_lo + kk;
+                const u2 c = k < p.K ? codes8(*(const u4*)(x + m * p.K + k)) : u2{0, 0};
+                *(u2*)(aq_lds + m * slice + kk) = c;
+            }
         }
         __syncthreads();
     } else if constexpr (V == V_FP8 || V == V_FP8X) {
