@@ -1088,7 +1088,7 @@ static hipError_t launch_gemm_ks(const LinParams& p, hipStream_t stream) {
 
 
 // Kernel choice for the tiled path, from measured M=1024 sweeps on the
-// Llama-3-8B projection shapes. "One tile per CU" shapes (at most 256
+// Llama-3-8B projection shapes (fp8) and K = N in 4096..8192 (W4A8). "One tile per CU" shapes (at most 256
 // 128x128 tiles) favour kernels that hide latency inside one block: the
 // k-split exact kernel and the register-prefetching fp8 kernel with a
 // three-stage ring; shapes with many 256x256 tiles favour the big fp8 tile.
@@ -1104,8 +1104,8 @@ static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
         if (t128 <= CUS) return launch_gemm_pipe<V, 128, 128, 4, 2, 3>(p, stream);
         if (t256 >= 3 * CUS / 2) return launch_gemm<V, 256, 256, 4, 4, 2>(p, stream);
         return launch_gemm<V, 128, 128, 2, 4, 2>(p, stream);
-    } else {
-        return launch_gemm<V, 128, 128, 2, 2, 2>(p, stream);
+    } else {  // W4A8: best at every K = N in 4096..8192 measured
+        return launch_gemm_pipe<V, 128, 128, 2, 4, 2>(p, stream);
     }
 }
 

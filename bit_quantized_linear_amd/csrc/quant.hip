@@ -137,13 +137,7 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
 // the weights use: tiles of 16 rows x 128 k (2048 B), all k-tiles of a
 // 16-row strip consecutive, a tile stored as [half h][lane l][16 B] with
 // row l % 16 and k = 32*(l/16) + 16*h + j.  Columns k >= K up to the tile
-// edge hold zero codes; rows past M in the last strip are never stored to
-// an output and are left unwritten.
-
-__device__ __forceinline__ int64_t packed_offset(int64_t m, int64_t k, int64_t KT) {
-    return ((m >> 4) * KT + (k >> 7)) * 2048 + ((k >> 4) & 1) * 1024 +
-           ((m & 15) + 16 * ((k >> 5) & 3)) * 16 + (k & 15);
-}
+// edge and rows past M in the last strip hold zero codes.
 
 // the tile loop of cast_e4m3_packed_kernel, for a given x -> x/s
 template <int DT, class Div>
@@ -211,16 +205,26 @@ __global__ __launch_bounds__(QT) void cast_e4m3_packed_kernel(const uint16_t* __
         cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, [&](float v) { return v / s; });
 }
 
-// Row-major 8-bit codes [M, K] -> packed layout; grid-stride over 16-byte
-// items (KT*8 per row, the padding up to the tile edge included).
+// Row-major 8-bit codes [M, K] -> packed layout: one wave per 16 x 128
+// tile (grid-stride), lane l = r + 16 g moving row 16 mt + r, k = 128 kt +
+// 32 g .. +31 (two 16-byte loads) to tile + 16 l and tile + 1024 + 16 l, so
+// each wave reads 128 contiguous bytes per row and stores two contiguous
+// 1 KiB runs. Rows past M and k past K (a multiple of 16) become zero codes.
 __global__ __launch_bounds__(QT) void pack_codes_kernel(const uint8_t* __restrict__ src, int64_t M,
                                                         int64_t K, int64_t KT,
                                                         uint8_t* __restrict__ dst) {
-    const int64_t per_row = KT * 8, total = M * per_row;
-    for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < total; i += (int64_t)gridDim.x * QT) {
-        const int64_t m = i / per_row, k = (i % per_row) * 16;
-        const u4 v = k < K ? *(const u4*)(src + m * K + k) : u4{0, 0, 0, 0};
-        *(u4*)(dst + packed_offset(m, k, KT)) = v;
+    constexpr int WPB = QT / 64;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int64_t tiles = ((M + 15) / 16) * KT;
+    for (int64_t t = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6); t < tiles;
+         t += (int64_t)gridDim.x * WPB) {
+        const int64_t m = (t / KT) * 16 + r, k = (t % KT) * 128 + 32 * g;
+        const bool row = m < M;
+        const u4 lo = row && k < K ? *(const u4*)(src + m * K + k) : u4{0, 0, 0, 0};
+        const u4 hi = row && k + 16 < K ? *(const u4*)(src + m * K + k + 16) : u4{0, 0, 0, 0};
+        uint8_t* tile = dst + t * 2048 + lane * 16;
+        *(u4*)tile = lo;
+        *(u4*)(tile + 1024) = hi;
     }
 }
 
@@ -250,7 +254,7 @@ hipError_t launch_quant_dynamic_packed(const void* x, int xdt, int64_t M, int64_
 hipError_t launch_pack_codes(const uint8_t* src, int64_t M, int64_t K, uint8_t* dst,
                              hipStream_t stream) {
     const int64_t KT = (K + 127) / 128;
-    int64_t blocks = (M * KT * 8 + QT - 1) / QT;
+    int64_t blocks = (((M + 15) / 16) * KT + QT / 64 - 1) / (QT / 64);
     if (blocks > 8192) blocks = 8192;
     pack_codes_kernel<<<(unsigned)blocks, QT, 0, stream>>>(src, M, K, KT, dst);
     return hipGetLastError();
