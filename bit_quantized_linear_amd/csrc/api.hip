@@ -258,17 +258,20 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
         return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
     }
     const float* sa = a_scale;
-    hipError_t e;
+    // pre-quantized A on the small-M path is read row-major where it is
+    const bool direct = adt == BQL_E4M3 && bql::use_small_m(variant, M, N, K);
+    hipError_t e = hipSuccess;
     if (adt != BQL_E4M3) {
         e = bql::launch_quant_dynamic_packed(a, adt, M, K, aq, a_scale, wsb, s);
         sa = (const float*)(wsb + 4096);
-    } else {
+    } else if (!direct) {
         e = bql::launch_pack_codes((const uint8_t*)a, M, K, aq, s);
     }
     if (e != hipSuccess) return hip_status(e);
     bql::LinearArgs la;
     la.variant = variant;
-    la.a = aq;
+    la.a = direct ? a : aq;
+    la.a_rowmajor = direct ? 1 : 0;
     la.w = (const uint8_t*)w_packed;
     la.M = M;
     la.N = N;
@@ -341,11 +344,16 @@ bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* 
     }
     CHECK(need_ws(ws, ws_bytes, bql_w4a8_linear_workspace_size(M, N, K)));
     uint8_t* aq_ws = (uint8_t*)ws;
-    hipError_t e = bql::launch_pack_codes((const uint8_t*)aq, M, K, aq_ws, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e);
+    // the small-M path reads the row-major int8 A where it is
+    const bool direct = bql::use_small_m(bql::V_W4A8, M, N, K);
+    if (!direct) {
+        hipError_t e = bql::launch_pack_codes((const uint8_t*)aq, M, K, aq_ws, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
     bql::LinearArgs la;
     la.variant = bql::V_W4A8;
-    la.a = aq_ws;
+    la.a = direct ? (const void*)aq : (const void*)aq_ws;
+    la.a_rowmajor = direct ? 1 : 0;
     la.w = (const uint8_t*)w_packed;
     la.M = M;
     la.N = N;

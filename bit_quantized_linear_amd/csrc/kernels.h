@@ -75,6 +75,8 @@ struct LinearArgs {
     int xdt = 0;
     float* scale_out = nullptr;  // optional copy of sA for the caller
     float* scale_ws = nullptr;   // sA in the workspace (read by the split-K reduce)
+    // small-M path only: 8-bit A is read row-major [M, K] (no repack launch)
+    int a_rowmajor = 0;
 };
 
 // Whether an fp8 call with dynamic quantization runs the fused small-M kernel.

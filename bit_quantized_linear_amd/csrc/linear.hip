@@ -38,6 +38,7 @@ struct LinParams {
     int xdt;                // fused quantization: IN_F16 / IN_BF16
     float* scale_out;       // fused quantization: optional copy of sA for the caller
     float* scale_ws;        // fused quantization: sA for the split-K reduce
+    int a_rowmajor;         // small-M kernels: 8-bit A is row-major [M, K], not packed
 };
 
 template <int V> struct VT;
@@ -70,27 +71,61 @@ template <> struct VT<V_W4A8> {
     using E = int;
 };
 
-// One lane's A operand for k-tile kt of row tile mt.  Packed 8-bit A: the
-// lane's 32 bytes are at tile + lane*16 and tile + 1024 + lane*16.  W8A16:
-// row-major fp16, row `row`, k0 .. k0+31 with k0 = 128 kt + 32 (lane/16),
-// zero where the row or k does not exist.
+// A operand of the small-M kernels, read through a buffer descriptor over
+// one 16-row tile of A (rows past M lie outside it and read as zero; k past
+// K gets an out-of-range offset), so every load is unconditional.
+//   W8A16: row-major fp16; lane l takes row l%16, k0 .. k0+31 with
+//          k0 = 128 kt + 32 (l/16), as four 16-byte loads.
+//   8-bit row-major (small M): the lane's 32 bytes of the operand tile,
+//          row l%16, k0 .. k0+31, as two 16-byte loads.
+//   8-bit packed: the lane's two 16-byte chunks of the 2 KiB tile.
 template <int V>
-__device__ __forceinline__ void load_a(u4 (&f)[VT<V>::A_CHUNKS], const LinParams& p, int64_t mt,
-                                       int64_t kt, int lane, bool ok) {
-    if constexpr (V == V_W8A16) {
-        const int64_t row = mt * 16 + (lane & 15);
-        const int64_t k0 = kt * TILE_K + 32 * (lane >> 4);
-        const uint16_t* q = (const uint16_t*)p.a + row * p.K + k0;
-        ok = ok && row < p.M;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            f[c] = (ok && k0 + 8 * c < p.K) ? *(const u4*)(q + 8 * c) : u4{0, 0, 0, 0};
-    } else {
-        const uint8_t* t = (const uint8_t*)p.a + (mt * p.KT + kt) * 2048 + lane * 16;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) f[c] = ok ? *(const u4*)(t + 1024 * c) : u4{0, 0, 0, 0};
+struct ALoader {
+    __amdgpu_buffer_rsrc_t rs;
+    int64_t rows;
+    __device__ ALoader(const LinParams& p, int64_t mt) {
+        const int64_t left = p.M - mt * 16;
+        rows = left < 16 ? left : 16;
+        const uint8_t* base;
+        int64_t bytes;
+        if (V == V_W8A16) {
+            base = (const uint8_t*)p.a + mt * 16 * p.K * 2;
+            bytes = rows * p.K * 2;
+        } else if (p.a_rowmajor) {
+            base = (const uint8_t*)p.a + mt * 16 * p.K;
+            bytes = rows * p.K;
+        } else {
+            base = (const uint8_t*)p.a + mt * p.KT * 2048;
+            bytes = p.KT * 2048;
+        }
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
     }
-}
+    __device__ __forceinline__ void load(u4 (&f)[VT<V>::A_CHUNKS], const LinParams& p, int64_t kt,
+                                         int lane, bool ok) const {
+        constexpr uint32_t OOB = 0x7FFFFFF0u;
+        const int64_t r = lane & 15, k0 = kt * TILE_K + 32 * (lane >> 4);
+        if constexpr (V == V_W8A16) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool v = ok && k0 + 8 * c < p.K;
+                f[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs, (int)(v ? (uint32_t)((r * p.K + k0 + 8 * c) * 2) : OOB), 0, 0));
+            }
+        } else if (p.a_rowmajor) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bool v = ok && k0 + 16 * c < p.K;
+                f[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs, (int)(v ? (uint32_t)(r * p.K + k0 + 16 * c) : OOB), 0, 0));
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                f[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs, (int)(ok ? (uint32_t)(kt * 2048 + 1024 * c + lane * 16) : OOB), 0, 0));
+        }
+    }
+};
 
 template <int V>
 __device__ __forceinline__ void load_b(u4 (&f)[VT<V>::B_CHUNKS], const uint8_t* tile, int lane,
@@ -199,19 +234,52 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
     const int64_t kt_end = kt_begin + p.kt_per_split < p.KT ? kt_begin + p.kt_per_split : p.KT;
     const int g = lane >> 4;
 
-    // Weight tiles for k-tiles kt, kt + WAVES, ... (U of them) of this wave.
+    // Loads below are unconditional buffer loads: an offset past the
+    // descriptor's range reads zeros without touching memory, so no load sits
+    // in a branch and the compiler's waits count exactly the loads a value
+    // needs (a branch around a load makes it wait for every load).
+    constexpr uint32_t OOB = 0x7FFFFFF0u;
+    const int64_t strips = ntiles - nt0 < NT ? ntiles - nt0 : NT;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + nt0 * p.KT * BT), (short)0, (int)(strips * p.KT * BT), 0x00020000);
+    // Weight tiles for k-tiles kt, kt + WAVES, ... (U of them) of this wave;
+    // tiles past this split's k range (or past N) read as zero.
     auto load_batch = [&](int64_t kt, u4 (&b)[U][NT][VT<V>::B_CHUNKS]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = kt + u * WAVES;
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
-                load_b<V>(b[u][j], p.w + ((nt0 + j) * p.KT + k) * BT, lane,
-                          k < kt_end && (nt0 + j) < ntiles);
+            for (int j = 0; j < NT; ++j) {
+                const bool ok = k < kt_end && j < strips;
+                const uint32_t off = (uint32_t)((j * p.KT + k) * BT) + lane * 16;
+#pragma unroll
+                for (int c = 0; c < VT<V>::B_CHUNKS; ++c)
+                    b[u][j][c] = __builtin_bit_cast(
+                        u4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ok ? off + c * 1024 : OOB), 0, 2));
+            }
         }
     };
-    // The first batch of weights is requested before anything else, so its
-    // HBM latency overlaps the scale computation and the A cast below.
+    // FUSED with one K split (the block's slice is all of A): the first
+    // HOLD*T vectors of A are loaded once, before the weights, and kept for
+    // the cast. Loads retire in issue order, so A issued first arrives
+    // without waiting for the weight tiles behind it. (With several splits
+    // the held vectors still feed the amax; the cast reloads its slice.)
+    constexpr int T = 64 * WAVES, HOLD = FUSED ? 4 : 1;
+    const bool whole = FUSED && p.splits == 1;
+    const int64_t nvec = p.M * p.K / 8;  // K is a multiple of 16
+    u4 held[HOLD];
+    if constexpr (FUSED) {
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)p.a, (short)0, (int)(nvec * 16), 0x00020000);
+#pragma unroll
+        for (int h = 0; h < HOLD; ++h) {
+            const int64_t i = threadIdx.x + (int64_t)h * T;
+            held[h] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ra, (int)(i < nvec ? i * 16 : OOB), 0, 0));
+        }
+    }
+    // The first batch of weights is requested next, so its HBM latency
+    // overlaps the scale computation and the A cast below.
     u4 bq[U][NT][VT<V>::B_CHUNKS];
     load_batch(kt_begin + wave, bq);
 
@@ -219,8 +287,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
     if constexpr (FUSED) {
         __shared__ uint32_t sh[16];
         const uint16_t* x = (const uint16_t*)p.a;
-        const int64_t nvec = p.M * p.K / 8;  // K is a multiple of 16
-        constexpr int T = 64 * WAVES, HOLD = 4;
         uint32_t mb = 0;
         auto fold = [&](const u4& v) {
 #pragma unroll
@@ -230,18 +296,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
                 mb = mb > hi ? mb : hi;
             }
         };
-        // With one K split the block's slice is all of A: the first HOLD*T
-        // vectors are loaded once and kept for the cast.
-        const bool whole = p.splits == 1;
-        u4 held[HOLD];
-#pragma unroll
-        for (int h = 0; h < HOLD; ++h) {
-            const int64_t i = threadIdx.x + (int64_t)h * T;
-            held[h] = whole && i < nvec ? ((const u4*)x)[i] : u4{0, 0, 0, 0};
-        }
 #pragma unroll
         for (int h = 0; h < HOLD; ++h) fold(held[h]);
-        for (int64_t i = threadIdx.x + (whole ? (int64_t)HOLD * T : 0); i < nvec; i += T) fold(((const u4*)x)[i]);
+        for (int64_t i = threadIdx.x + (int64_t)HOLD * T; i < nvec; i += T) fold(((const u4*)x)[i]);
         mb = block_max_u32(mb, sh);
         const float amax = p.xdt == IN_BF16 ? to_f32<IN_BF16>(mb) : to_f32<IN_F16>(mb);
         sa = amax == 0.0f ? 1.0f : amax / 448.0f;  // IEEE division, as the standalone quantizer
@@ -290,12 +347,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
     Acc acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = Acc{0, 0, 0, 0};
+    const ALoader<V> aload(p, mt);
 
     // Register double buffering: the next batch is in flight while this
-    // one is multiplied.
+    // one is multiplied. The batch loads are unconditional: tiles past this
+    // split's range read as zero without touching memory, and a branch
+    // around them would make the loads of A below wait for the whole batch.
     for (int64_t kt = kt_begin + wave; kt < kt_end; kt += WAVES * U) {
         u4 bn[U][NT][VT<V>::B_CHUNKS];
-        if (kt + WAVES * U < kt_end) load_batch(kt + WAVES * U, bn);
+        load_batch(kt + WAVES * U, bn);
         u4 a[U][VT<V>::A_CHUNKS];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -308,7 +368,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
                 a[u][0] = ok ? *(const u4*)t : u4{0, 0, 0, 0};
                 a[u][1] = ok ? *(const u4*)(t + 16) : u4{0, 0, 0, 0};
             } else {
-                load_a<V>(a[u], p, mt, k, lane, kv);
+                aload.load(a[u], p, k, lane, kv);
             }
         }
 #pragma unroll
@@ -1128,6 +1188,7 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
     p.xdt = args.xdt;
     p.scale_out = args.scale_out;
     p.scale_ws = args.scale_ws;
+    p.a_rowmajor = args.a_rowmajor;
     if (use_small_m(args.variant, args.M, args.N, args.K)) {
         GemvPlan pl = plan_gemv(args.M, args.N, args.K);
         p.KT = pl.KT;
@@ -1145,6 +1206,7 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
             default: return run_gemv<V_W4A8, false>(p, pl.waves, stream);
         }
     }
+    if (args.a_rowmajor) return hipErrorInvalidValue;  // the tile kernels read packed A only
     p.KT = (args.K + TILE_K - 1) / TILE_K;
     p.kt_per_split = p.KT;
     p.splits = 1;
