@@ -43,6 +43,9 @@ PEAK_F16_TFLOPS = 2500.0
 PEAK_I8_TOPS = 5000.0
 SHAPES = wl.CFG3_SHAPES
 ROTATE_BYTES = 640 * 2 ** 20  # > 2 x 256 MiB Infinity Cache
+# steps per captured graph for the microsecond-scale small-M steps (M=1024
+# steps keep one per graph; a graph launch costs several microseconds)
+SMALL_STEPS_PER_GRAPH = 4
 
 
 CALIBRATION_COPY_BYTES = 256 * 2 ** 20
@@ -181,24 +184,37 @@ def time_steps(step, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def capture_graphs(step, n):
-    """One HIP graph per weight-rotation slot, each holding one whole step
-    (the step's kernels replay without host launch overhead, as a serving
-    loop under graph capture runs them)."""
+def capture_graphs(step, n, per_graph=1):
+    """HIP graphs over the weight-rotation slots: graph g holds steps
+    g*per_graph .. g*per_graph + per_graph - 1 back to back (the kernels
+    replay without host launch overhead, as a serving loop under graph
+    capture runs a whole decode step of many layers; per_graph > 1 keeps
+    the launch of one graph from dominating steps of a few microseconds)."""
+    ngraphs = max(1, -(-n // per_graph))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(n):
+        for i in range(ngraphs * per_graph):
             step(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = []
-    for i in range(n):
+    for gi in range(ngraphs):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(i)
+            for t in range(per_graph):
+                step(gi * per_graph + t)
         graphs.append(g)
     return graphs
+
+
+def graph_step_time(step, n, steps, warmup, per_graph=1):
+    """Seconds per step from replaying the graphs of capture_graphs: at
+    least `steps` steps are timed (a whole number of graphs)."""
+    graphs = capture_graphs(step, n, per_graph)
+    reps = max(1, -(-steps // per_graph))
+    sec = time_steps(lambda i: graphs[i % len(graphs)].replay(), reps, max(1, -(-warmup // per_graph)))
+    return sec / per_graph
 
 
 def event_avg_us(launch, n):
@@ -252,9 +268,8 @@ def rotation(pw, bql, nbytes):
     return [bql.PackedWeight(pw.packed.clone(), pw.scales.clone(), pw.N, pw.K, pw.fmt) for _ in range(n)]
 
 
-def timed_graphs(step, nslots, steps, warmup):
-    graphs = capture_graphs(step, nslots)
-    return time_steps(lambda i: graphs[i % nslots].replay(), steps, warmup)
+def timed_graphs(step, nslots, steps, warmup, per_graph=1):
+    return graph_step_time(step, nslots, steps, warmup, per_graph)
 
 
 def bench_w8a16(bql, dev, steps, warmup):
@@ -274,7 +289,8 @@ def bench_w8a16(bql, dev, steps, warmup):
         a = torch.from_numpy(wl.activation(wl.rng(2, M, 3), M, K, "f16").view(np.int16)).to(dev).view(torch.float16)
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         ws = torch.empty(max(256, bql.lib().bql_w8a16_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=dev)
-        sec = timed_graphs(lambda i: bql.w8a16_linear(a, rot[i % len(rot)], out=y, ws=ws), len(rot), steps, warmup)
+        sec = timed_graphs(lambda i: bql.w8a16_linear(a, rot[i % len(rot)], out=y, ws=ws), len(rot), steps, warmup,
+                           per_graph=SMALL_STEPS_PER_GRAPH * 2)
         byts = N * K + 2 * N + 2 * M * K + 2 * M * N
         gbs = byts / sec / 1e9
         out[f"M{M}"] = {"value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(sec * 1e6, 2),
@@ -317,7 +333,7 @@ def bench_w4a8(bql, dev, steps, warmup):
             for j in range(len(shapes)):
                 r = rots[j]
                 bql.w4a8_linear(aqs[j], sas[j], r[i % len(r)], out=ys[j], ws=wss[j])
-        sec = timed_graphs(step, nslots, steps, warmup)
+        sec = timed_graphs(step, nslots, steps, warmup, per_graph=1 if M > 16 else SMALL_STEPS_PER_GRAPH)
         ops = sum(2 * M * n * n for n in shapes)
         byts = sum(n * n // 2 + M * n + 4 * M + 2 * n + 2 * M * n for n in shapes)
         if M == 1:
@@ -384,8 +400,8 @@ def main():
         sec = sec_eager = float("nan")
         if timed:
             sec_eager = time_steps(step, args.steps, args.warmup)
-            graphs = capture_graphs(step, nrot)
-            sec = time_steps(lambda i: graphs[i % nrot].replay(), args.steps, args.warmup)
+            sec = graph_step_time(step, nrot, args.steps, args.warmup,
+                                  per_graph=1 if M > 16 else SMALL_STEPS_PER_GRAPH)
         flops = sum(2 * M * N * K for N, K in SHAPES)
         byts = sum(algorithmic_bytes(M, N, K) for N, K in SHAPES)
         return abits, pre, outs, wss, (sec, sec_eager), flops, byts
@@ -463,7 +479,9 @@ def main():
                         "dynamic per-tensor E4M3 activation scale, per-tensor E4M3 weights, "
                         "exact fp32 accumulation, bf16 out",
             "M": M, "accum": "exact", "weight_rotation_copies": nrot,
-            "timing": "HIP graph replay of whole steps (eager-launch rates under 'eager')",
+            "timing": "HIP graph replay of whole steps, one step per graph at M=1024 and "
+                      f"{SMALL_STEPS_PER_GRAPH} consecutive steps per graph at M=1 (each on its own "
+                      "weight copy); eager-launch rates under 'eager'",
         },
         "eager": {"value": round(flops / sec_eager / 1e12, 2), "unit": "TFLOP/s",
                   "m1_GBs": round(byts1 / sec1_eager / 1e9, 1),
@@ -474,7 +492,7 @@ def main():
             "ms_per_pass": round(sec1 * 1e3, 4),
             "gemm_only_GBs": round(byts1 / sec1p / 1e9, 1),
             "note": "M=1, four linears, dynamic quant included (one fused kernel per linear); "
-                    "gemm_only = pre-quantized A (repack + streaming kernel)",
+                    "gemm_only = pre-quantized E4M3 A (the streaming kernel alone)",
         },
         "fast_accum": {
             "value": round(flops / sec_f / 1e12, 2), "unit": "TFLOP/s",
