@@ -240,6 +240,28 @@ def test_prequantized_input_and_scale_interleave(M):
     assert_close(host_f64(y_c), y_ref, f"pre-quantized M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_prequantized_small_m_half_tiles(M):
+    # Pre-quantized A on the small-M path is read row-major; K = 144 leaves
+    # the second 16-byte half of some lanes' 32-k chunk past K (zeros).
+    g = np.random.Generator(np.random.PCG64(34 + M))
+    N, K = 48, 144
+    aq = _random_codes(g, (M, K))
+    wq = _random_codes(g, (N, K))
+    sa, sw = np.float32(0.5), np.float32(0.25)
+    pw = bql.prepack_weight(dev(wq), "fp8_tensor", scales=torch.tensor([sw], device=DEV))
+    for fast in (False, True):
+        y = bql.fp8_linear(dev(aq).view(torch.float8_e4m3fn), pw, a_scale=torch.tensor([sa], device=DEV),
+                           out_dtype=torch.float32, fast_accum=fast)
+        torch.cuda.synchronize()
+        y_ref = oracle.fp8_linear(aq, sa, wq, np.array([sw], dtype=np.float32))
+        if fast:
+            abs_sum = oracle.fp8_acc(aq & 0x7F, wq & 0x7F) * np.float64(sa) * np.float64(sw)
+            assert_fast_bound(host_f64(y), y_ref, abs_sum, f"pre-quantized small M={M} fast")
+        else:
+            assert_close(host_f64(y), y_ref, f"pre-quantized small M={M}")
+
+
 @pytest.mark.parametrize("fast", [False, True])
 @pytest.mark.parametrize("M", [1, 16, 1024])
 def test_deterministic(M, fast):
