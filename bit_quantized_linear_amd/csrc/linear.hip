@@ -4,21 +4,27 @@
 //
 // Two regimes, as the micro-benchmark on vLLM PR #4118 shows (small token
 // counts are a weight-streaming problem, large ones a matrix-core problem):
-//   * small M (<= 16 rows of A): a streaming kernel.  Each wave walks k-tiles
-//     of a 16-channel weight strip, loading every MFMA operand straight from
-//     HBM with 16-byte loads (the packed layout makes one wave-wide load
-//     1 KiB contiguous), A rows padded to 16.  Waves of a block split K and
-//     are summed through LDS in a fixed order; blocks may split K further,
-//     with partials summed in a fixed order by a second kernel.
-//     Deterministic, no atomics.
-//   * large M: a block-tiled MFMA kernel.  Both operands live in HBM in the
+//   * small M (<= 16 rows of A; W8A16 at every M): a streaming kernel.  Each
+//     wave walks k-tiles of a 16-channel weight strip, loading every MFMA
+//     operand straight from HBM with unconditional 16-byte buffer loads (the
+//     packed layout makes one wave-wide load 1 KiB contiguous; offsets past
+//     a descriptor's range read zeros).  A is read where it is: fp16
+//     row-major (W8A16), 8-bit row-major (pre-quantized fp8 / int8), or
+//     quantized by the kernel itself into LDS (fp8 with dynamic scaling,
+//     M <= 4).  Waves of a block split K and are summed through LDS in a
+//     fixed order; blocks may split K further, with partials summed in a
+//     fixed order by a second kernel.  Deterministic, no atomics.
+//   * large M: block-tiled MFMA kernels.  Both operands live in HBM in the
 //     MFMA operand tile layout (weights by prepack, 8-bit activations by
 //     the quantizer or a repack), so each 1 KiB of a stage is one
 //     buffer_load ... lds instruction that writes LDS directly (no VGPR
-//     staging, no address scatter).  A ring of S stages keeps S-1 k-tiles
-//     in flight; waits on the vector-memory counter are explicit because the
-//     compiler does not track these LDS writes.  The epilogue converts and
-//     stages each 16-row band through LDS and writes it with 16-byte stores.
+//     staging, no address scatter).  A ring of S stages keeps k-tiles in
+//     flight; waits on the vector-memory counter are explicit because the
+//     compiler does not track these LDS writes.  Output tiles are handed to
+//     the 8 XCDs in contiguous ranges.  The epilogue converts and stages
+//     each 16-row band through LDS and writes it with 16-byte stores.
+//     Three main loops (plain, register-prefetching, k-split) are chosen
+//     per shape by run_gemm.
 #include <atomic>
 
 #include "device.h"
@@ -27,8 +33,9 @@
 namespace bql {
 
 struct LinParams {
-    const void* a;          // packed 8-bit A (fp8 / int8 variants) or row-major fp16 (W8A16);
-                            // row-major fp16/bf16 when the small-M kernel quantizes A itself
+    const void* a;          // packed 8-bit A (fp8 / int8 variants), row-major 8-bit A (small M,
+                            // a_rowmajor), row-major fp16 (W8A16), or row-major fp16/bf16
+                            // when the small-M kernel quantizes A itself
     const uint8_t* w;
     int64_t M, N, K, KT;
     int64_t kt_per_split;
@@ -126,15 +133,6 @@ struct ALoader {
         }
     }
 };
-
-template <int V>
-__device__ __forceinline__ void load_b(u4 (&f)[VT<V>::B_CHUNKS], const uint8_t* tile, int lane,
-                                       bool ok) {
-#pragma unroll
-    for (int c = 0; c < VT<V>::B_CHUNKS; ++c)
-        f[c] = ok ? __builtin_nontemporal_load((const u4*)(tile + c * 1024 + lane * 16))
-                  : u4{0, 0, 0, 0};
-}
 
 __device__ __forceinline__ v8i as_v8i(const u4& x0, const u4& x1) {
     return v8i{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
