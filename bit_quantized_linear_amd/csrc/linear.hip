@@ -1194,8 +1194,12 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
         p.splits = pl.splits;
         if (args.fused) {
             p.ep.a_scale = args.scale_ws;  // read by the split-K reduce
-            if (args.variant == V_FP8) return run_gemv<V_FP8, true>(p, pl.waves, stream);
-            return run_gemv<V_FP8X, true>(p, pl.waves, stream);
+            // Fused blocks first reduce the amax over all of A and cast it
+            // with every thread, behind block-wide barriers; 8 waves per
+            // block (each then streams twice the k-tiles, same split plan)
+            // measured 7 % faster at M = 1 than the plan's 16.
+            if (args.variant == V_FP8) return run_gemv<V_FP8, true>(p, 8, stream);
+            return run_gemv<V_FP8X, true>(p, 8, stream);
         }
         switch (args.variant) {
             case V_FP8: return run_gemv<V_FP8, false>(p, pl.waves, stream);
