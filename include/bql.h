@@ -39,7 +39,8 @@
  *     kept for bql_last_error() (per thread).  A failure reported by the HIP
  *     runtime at launch returns BQL_ERR_HIP.
  *   - Workspaces are caller-owned device buffers of at least the size the
- *     matching *_workspace_size() function returns; their content on entry
+ *     matching *_workspace_size() function returns, 256-byte aligned (else
+ *     BQL_ERR_ALIGN; a size of 0 needs no buffer); their content on entry
  *     does not matter and is garbage on exit.  Calls that overlap in time
  *     must not share a workspace.
  *   - No entry point may be called concurrently with another call that
