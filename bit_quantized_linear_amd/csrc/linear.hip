@@ -80,7 +80,10 @@ template <> struct VT<V_W4A8> {
 
 // A operand of the small-M kernels, read through a buffer descriptor over
 // one 16-row tile of A (rows past M lie outside it and read as zero; k past
-// K gets an out-of-range offset), so every load is unconditional.
+// K or past the block's split of K gets an out-of-range offset and reads zero
+// too).  The layout is fixed per call, so the lane's offsets are set
+// up once as base + kt * per-k-tile stride + chunk stride and every load in
+// the loop is an unconditional buffer load.
 //   W8A16: row-major fp16; lane l takes row l%16, k0 .. k0+31 with
 //          k0 = 128 kt + 32 (l/16), as four 16-byte loads.
 //   8-bit row-major (small M): the lane's 32 bytes of the operand tile,
@@ -88,48 +91,47 @@ template <> struct VT<V_W4A8> {
 //   8-bit packed: the lane's two 16-byte chunks of the 2 KiB tile.
 template <int V>
 struct ALoader {
+    static constexpr int CH = VT<V>::A_CHUNKS;
+    static constexpr int KC = V == V_W8A16 ? 8 : 16;  // k per 16-byte chunk
     __amdgpu_buffer_rsrc_t rs;
-    int64_t rows;
-    __device__ ALoader(const LinParams& p, int64_t mt) {
+    uint32_t base, skt, sc;  // lane's byte offset at kt = 0; strides per k-tile and per chunk
+    int64_t kcol, klim;      // k of the lane's first element at kt = 0; chunks at k >= klim read zero
+    __device__ ALoader(const LinParams& p, int64_t mt, int lane, int64_t kt_end) {
         const int64_t left = p.M - mt * 16;
-        rows = left < 16 ? left : 16;
-        const uint8_t* base;
+        const int64_t rows = left < 16 ? left : 16;
+        const int64_t r = lane & 15;
+        kcol = 32 * (lane >> 4);
+        klim = kt_end * TILE_K < p.K ? kt_end * TILE_K : p.K;
+        const uint8_t* ptr;
         int64_t bytes;
         if (V == V_W8A16) {
-            base = (const uint8_t*)p.a + mt * 16 * p.K * 2;
+            ptr = (const uint8_t*)p.a + mt * 16 * p.K * 2;
             bytes = rows * p.K * 2;
+            base = (uint32_t)((r * p.K + kcol) * 2);
+            skt = TILE_K * 2;
+            sc = 16;
         } else if (p.a_rowmajor) {
-            base = (const uint8_t*)p.a + mt * 16 * p.K;
+            ptr = (const uint8_t*)p.a + mt * 16 * p.K;
             bytes = rows * p.K;
+            base = (uint32_t)(r * p.K + kcol);
+            skt = TILE_K;
+            sc = 16;
         } else {
-            base = (const uint8_t*)p.a + mt * p.KT * 2048;
+            ptr = (const uint8_t*)p.a + mt * p.KT * 2048;
             bytes = p.KT * 2048;
+            base = (uint32_t)(lane * 16);
+            skt = 2048;
+            sc = 1024;
         }
-        rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, (int)bytes, 0x00020000);
     }
-    __device__ __forceinline__ void load(u4 (&f)[VT<V>::A_CHUNKS], const LinParams& p, int64_t kt,
-                                         int lane, bool ok) const {
+    __device__ __forceinline__ void load(u4 (&f)[CH], int64_t kt) const {
         constexpr uint32_t OOB = 0x7FFFFFF0u;
-        const int64_t r = lane & 15, k0 = kt * TILE_K + 32 * (lane >> 4);
-        if constexpr (V == V_W8A16) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bool v = ok && k0 + 8 * c < p.K;
-                f[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs, (int)(v ? (uint32_t)((r * p.K + k0 + 8 * c) * 2) : OOB), 0, 0));
-            }
-        } else if (p.a_rowmajor) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bool v = ok && k0 + 16 * c < p.K;
-                f[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs, (int)(v ? (uint32_t)(r * p.K + k0 + 16 * c) : OOB), 0, 0));
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                f[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs, (int)(ok ? (uint32_t)(kt * 2048 + 1024 * c + lane * 16) : OOB), 0, 0));
+        for (int c = 0; c < CH; ++c) {
+            const bool v = kcol + kt * TILE_K + KC * c < klim;
+            const uint32_t off = base + (uint32_t)kt * skt + c * sc;
+            f[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(v ? off : OOB), 0, 0));
         }
     }
 };
@@ -218,8 +220,15 @@ __device__ __forceinline__ int out_size(int ydt) {
 // reads all of A for the per-tensor amax (a max, so every block gets the
 // same scale bit for bit), then casts the A slice its K split needs into
 // LDS as [M][slice] codes.  One launch instead of amax, cast and GEMV.
+// Occupancy the small-M kernels are compiled for (waves per SIMD): enough
+// register room for two weight batches, A and the decoded operands without
+// spilling, and as many resident blocks as that leaves.
+constexpr int gemv_min_waves(int v, bool fused) {
+    return (fused || v == V_FP8 || v == V_W4A8) ? 6 : 5;
+}
+
 template <int V, int NT, int WAVES, int U, bool FUSED>
-__global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv_min_waves(V, FUSED), 8))) void gemv_kernel(LinParams p) {
     using Acc = typename VT<V>::Acc;
     constexpr int BT = VT<V>::B_TILE;
     extern __shared__ __attribute__((aligned(16))) uint8_t aq_lds[];
@@ -304,39 +313,51 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
             if (p.scale_out) *p.scale_out = sa;
             if (p.scale_ws) *p.scale_ws = sa;
         }
-        auto codes8 = [&](const u4& v) {
+        // x / sA as the standalone quantizer forms it: from the reciprocal
+        // with one residual correction where that is the IEEE quotient's code
+        // for every input (the scale's range check), else the IEEE division.
+        auto codes8 = [&](const u4& v, auto div) {
             uint32_t c[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t lo = v[j] & 0xFFFFu, hi = v[j] >> 16;
-                c[2 * j] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)) / sa);
-                c[2 * j + 1] = e4m3_encode((p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)) / sa);
+                c[2 * j] = e4m3_encode(div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)));
+                c[2 * j + 1] = e4m3_encode(div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)));
             }
             return u2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                       c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
         };
-        const int64_t slice = p.kt_per_split * TILE_K, k_lo = kt_begin * TILE_K;
-        if (whole) {
-            // slice = [0, KT*128): cast the K real columns, zero the padding
-            const int64_t vpr = p.K / 8;  // vectors per row
+        // A is small here (at most a few rows of K), so 32-bit indices
+        const uint32_t slice = (uint32_t)(p.kt_per_split * TILE_K), k_lo = (uint32_t)(kt_begin * TILE_K);
+        const uint32_t nv = (uint32_t)nvec, kk_ = (uint32_t)p.K, mm = (uint32_t)p.M;
+        auto cast_all = [&](auto div) {
+            if (whole) {
+                // slice = [0, KT*128): cast the K real columns, zero the padding
+                const uint32_t vpr = kk_ / 8;  // vectors per row
 #pragma unroll
-            for (int h = 0; h < HOLD; ++h) {
-                const int64_t i = threadIdx.x + (int64_t)h * T;
-                if (i < nvec) *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(held[h]);
+                for (int h = 0; h < HOLD; ++h) {
+                    const uint32_t i = threadIdx.x + (uint32_t)h * T;
+                    if (i < nv) *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(held[h], div);
+                }
+                for (uint32_t i = threadIdx.x + (uint32_t)HOLD * T; i < nv; i += T)
+                    *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(((const u4*)x)[i], div);
+                const uint32_t pad = (slice - kk_) / 8;  // zero 8-byte items past K in each row
+                for (uint32_t i = threadIdx.x; i < mm * pad; i += T)
+                    *(u2*)(aq_lds + (i / pad) * slice + kk_ + (i % pad) * 8) = u2{0, 0};
+            } else {
+                const uint32_t items = mm * slice / 8;
+                for (uint32_t i = threadIdx.x; i < items; i += T) {
+                    const uint32_t m = i / (slice / 8), kk = (i % (slice / 8)) * 8, k = k_lo + kk;
+                    const u2 c = k < kk_ ? codes8(*(const u4*)(x + (size_t)m * kk_ + k), div) : u2{0, 0};
+                    *(u2*)(aq_lds + m * slice + kk) = c;
+                }
             }
-            for (int64_t i = threadIdx.x + (int64_t)HOLD * T; i < nvec; i += T)
-                *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(((const u4*)x)[i]);
-            const int64_t pad = (slice - p.K) / 8;  // zero 8-byte items past K in each row
-            for (int64_t i = threadIdx.x; i < p.M * pad; i += T)
-                *(u2*)(aq_lds + (i / pad) * slice + p.K + (i % pad) * 8) = u2{0, 0};
-        } else {
-            const int64_t items = p.M * slice / 8;
-            for (int64_t i = threadIdx.x; i < items; i += T) {
-                const int64_t m = i / (slice / 8), kk = (i % (slice / 8)) * 8, k = k_lo + kk;
-                const u2 c = k < p.K ? codes8(*(const u4*)(x + m * p.K + k)) : u2{0, 0};
-                *(u2*)(aq_lds + m * slice + kk) = c;
-            }
-        }
+        };
+        const float y = 1.0f / sa;
+        if (recip_div_ok(sa))
+            cast_all([&](float v) { return div_by_scale(v, sa, y); });
+        else
+            cast_all([&](float v) { return v / sa; });
         __syncthreads();
     } else if constexpr (V == V_FP8 || V == V_FP8X) {
         sa = *p.ep.a_scale;
@@ -345,40 +366,48 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(LinParams p) {
     Acc acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = Acc{0, 0, 0, 0};
-    const ALoader<V> aload(p, mt);
+    const ALoader<V> aload(p, mt, lane, kt_end);
 
-    // Register double buffering: the next batch is in flight while this
-    // one is multiplied. The batch loads are unconditional: tiles past this
-    // split's range read as zero without touching memory, and a branch
-    // around them would make the loads of A below wait for the whole batch.
-    for (int64_t kt = kt_begin + wave; kt < kt_end; kt += WAVES * U) {
-        u4 bn[U][NT][VT<V>::B_CHUNKS];
-        load_batch(kt + WAVES * U, bn);
+    // Register double buffering: the next batch is in flight while this one
+    // is multiplied, with the two register sets used in turn (a copy of the
+    // next batch into the current one would wait for it to arrive). Loads
+    // retire in issue order, so the A loads of a batch are issued before the
+    // next batch of weights: the multiply waits for A and its own batch only.
+    // Every load is unconditional (tiles past this split's range read as zero
+    // without touching memory): a branch around a load makes the compiler
+    // wait for all outstanding loads at the join.
+    auto step = [&](int64_t kt, const u4 (&cur)[U][NT][VT<V>::B_CHUNKS], u4 (&nxt)[U][NT][VT<V>::B_CHUNKS]) {
         u4 a[U][VT<V>::A_CHUNKS];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = kt + u * WAVES;
-            const bool kv = k < kt_end;
             if constexpr (FUSED) {
+                // rows past M and k-tiles past the split read a valid LDS
+                // address and are then replaced by zero
                 const int row = lane & 15;
-                const uint8_t* t = aq_lds + row * p.kt_per_split * TILE_K + (k - kt_begin) * TILE_K + 32 * g;
-                const bool ok = kv && row < p.M;
-                a[u][0] = ok ? *(const u4*)t : u4{0, 0, 0, 0};
-                a[u][1] = ok ? *(const u4*)(t + 16) : u4{0, 0, 0, 0};
+                const bool ok = k < kt_end && row < p.M;
+                const uint8_t* t = aq_lds + (ok ? row * p.kt_per_split * TILE_K + (k - kt_begin) * TILE_K + 32 * g : 0);
+                const u4 x0 = *(const u4*)t, x1 = *(const u4*)(t + 16);
+                a[u][0] = ok ? x0 : u4{0, 0, 0, 0};
+                a[u][1] = ok ? x1 : u4{0, 0, 0, 0};
             } else {
-                aload.load(a[u], p, k, lane, kv);
+                aload.load(a[u], k);
             }
         }
+        load_batch(kt + WAVES * U, nxt);
+        // keep the loads above the multiplies (the scheduler would sink them)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) mma<V>(acc[j], a[u], bq[u][j]);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int c = 0; c < VT<V>::B_CHUNKS; ++c) bq[u][j][c] = bn[u][j][c];
+            for (int j = 0; j < NT; ++j) mma<V>(acc[j], a[u], cur[u][j]);
+    };
+    // Two steps per trip; the second may lie past the split's range, where
+    // both operands read as zero.
+    u4 bo[U][NT][VT<V>::B_CHUNKS];
+    for (int64_t kt = kt_begin + wave; kt < kt_end; kt += 2 * WAVES * U) {
+        step(kt, bq, bo);
+        step(kt + WAVES * U, bo, bq);
     }
 
     if constexpr (WAVES > 1) {
@@ -1023,7 +1052,8 @@ __global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
 
 // ------------------------------------------------------------------ host
 
-constexpr int GEMV_U = 2;
+constexpr int GEMV_U = 2;       // weight k-tiles per wave per batch
+constexpr int GEMV_WAVES = 8;   // measured faster than 16 at every M = 1 Llama shape
 constexpr int MAX_SPLITS = 8;
 constexpr int SMALL_M = 16;
 constexpr int FUSED_M = 4;                 // small-M fp8 calls that quantize A in-kernel
@@ -1037,21 +1067,20 @@ bool use_small_m(int variant, int64_t M, int64_t N, int64_t K) {
 struct GemvPlan {
     int64_t KT, kt_per_split;
     int splits;
-    int waves;
 };
 
-// Enough waves in flight to cover HBM latency: about 16 per CU, each with
-// GEMV_U weight tiles outstanding.  Few 16-channel strips get 16 waves per
-// block before K is split across blocks.
+// Blocks of GEMV_WAVES waves stream one 16-channel strip each.  Few strips
+// (short N) would leave CUs idle, so K is split across blocks (with a
+// fixed-order reduce) until there are about 256 blocks, or 512 when K is
+// short (KT < 32), keeping at least 8 (4) k-tiles per split.
 static GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
     GemvPlan pl;
     pl.KT = (K + TILE_K - 1) / TILE_K;
     const int64_t groups = (N / TILE_N) * ((M + 15) / 16);
-    pl.waves = (groups >= 1024 || pl.KT < 32) ? 8 : 16;
+    const int64_t target = pl.KT < 32 ? 512 : 256, min_kt = pl.KT < 32 ? 4 : 8;
     int s = 1;
     if (M <= SMALL_M)
-        while (groups * s * pl.waves < 4096 && s * 2 <= MAX_SPLITS && pl.KT / (s * 2) >= pl.waves / 2)
-            s *= 2;
+        while (groups * s < target && s * 2 <= MAX_SPLITS && pl.KT / (s * 2) >= min_kt) s *= 2;
     pl.kt_per_split = (pl.KT + s - 1) / s;
     pl.splits = (int)((pl.KT + pl.kt_per_split - 1) / pl.kt_per_split);
     return pl;
@@ -1070,13 +1099,10 @@ bool fused_small_m(int64_t M, int64_t N, int64_t K) {
 }
 
 template <int V, bool FUSED>
-static hipError_t run_gemv(LinParams p, int waves, hipStream_t stream) {
+static hipError_t run_gemv(LinParams p, hipStream_t stream) {
     dim3 grid((unsigned)(p.N / TILE_N), (unsigned)p.splits, (unsigned)((p.M + 15) / 16));
     const size_t lds = FUSED ? (size_t)(p.M * p.kt_per_split * TILE_K) : 0;
-    if (waves == 16)
-        gemv_kernel<V, 1, 16, GEMV_U, FUSED><<<grid, 64 * 16, lds, stream>>>(p);
-    else
-        gemv_kernel<V, 1, 8, GEMV_U, FUSED><<<grid, 64 * 8, lds, stream>>>(p);
+    gemv_kernel<V, 1, GEMV_WAVES, GEMV_U, FUSED><<<grid, 64 * GEMV_WAVES, lds, stream>>>(p);
     if (p.splits > 1) {
         const int64_t total = p.M * p.N;
         splitk_reduce_kernel<V><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
@@ -1194,18 +1220,14 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
         p.splits = pl.splits;
         if (args.fused) {
             p.ep.a_scale = args.scale_ws;  // read by the split-K reduce
-            // Fused blocks first reduce the amax over all of A and cast it
-            // with every thread, behind block-wide barriers; 8 waves per
-            // block (each then streams twice the k-tiles, same split plan)
-            // measured 7 % faster at M = 1 than the plan's 16.
-            if (args.variant == V_FP8) return run_gemv<V_FP8, true>(p, 8, stream);
-            return run_gemv<V_FP8X, true>(p, 8, stream);
+            if (args.variant == V_FP8) return run_gemv<V_FP8, true>(p, stream);
+            return run_gemv<V_FP8X, true>(p, stream);
         }
         switch (args.variant) {
-            case V_FP8: return run_gemv<V_FP8, false>(p, pl.waves, stream);
-            case V_FP8X: return run_gemv<V_FP8X, false>(p, pl.waves, stream);
-            case V_W8A16: return run_gemv<V_W8A16, false>(p, pl.waves, stream);
-            default: return run_gemv<V_W4A8, false>(p, pl.waves, stream);
+            case V_FP8: return run_gemv<V_FP8, false>(p, stream);
+            case V_FP8X: return run_gemv<V_FP8X, false>(p, stream);
+            case V_W8A16: return run_gemv<V_W8A16, false>(p, stream);
+            default: return run_gemv<V_W4A8, false>(p, stream);
         }
     }
     if (args.a_rowmajor) return hipErrorInvalidValue;  // the tile kernels read packed A only
