@@ -95,6 +95,20 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
     return s | c;
 }
 
+// Two fp32 -> OCP E4M3 codes (a in bits 0-7, b in bits 8-15), the same codes
+// as e4m3_encode, with the gfx950 conversion instruction: the input is first
+// clamped to [-448, 448] with med3 (infinities saturate, zero keeps its sign;
+// a NaN becomes 448, which takes the NaN's sign back from copysign), the
+// conversion rounds to nearest even, and a NaN input then gets its low code
+// bit set (0x7E -> 0x7F, 0xFE -> 0xFF).  Compared with e4m3_encode on every
+// fp32 bit pattern in both positions.
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
+    const float ca = __builtin_copysignf(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f), a);
+    const float cb = __builtin_copysignf(__builtin_amdgcn_fmed3f(b, -448.0f, 448.0f), b);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+    return c | (a != a ? 1u : 0u) | (b != b ? 0x100u : 0u);
+}
+
 // ------------------------------------------------------------- reductions
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

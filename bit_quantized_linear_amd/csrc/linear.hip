@@ -317,15 +317,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
         // with one residual correction where that is the IEEE quotient's code
         // for every input (the scale's range check), else the IEEE division.
         auto codes8 = [&](const u4& v, auto div) {
-            uint32_t c[8];
+            uint32_t c[4];  // code pairs
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t lo = v[j] & 0xFFFFu, hi = v[j] >> 16;
-                c[2 * j] = e4m3_encode(div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)));
-                c[2 * j + 1] = e4m3_encode(div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)));
+                c[j] = e4m3_encode2(div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)),
+                                    div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)));
             }
-            return u2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+            return u2{c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
         };
         // A is small here (at most a few rows of K), so 32-bit indices
         const uint32_t slice = (uint32_t)(p.kt_per_split * TILE_K), k_lo = (uint32_t)(kt_begin * TILE_K);

@@ -108,13 +108,11 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
         for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
              i += (int64_t)gridDim.x * QT) {
             u4 v = __builtin_nontemporal_load(&xv[i]);
-            uint32_t c[8];
+            uint32_t c[4];  // code pairs
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[2 * j] = e4m3_encode(div(to_f32<DT>(v[j] & 0xFFFFu)));
-                c[2 * j + 1] = e4m3_encode(div(to_f32<DT>(v[j] >> 16)));
-            }
-            u2 o = {pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+            for (int j = 0; j < 4; ++j)
+                c[j] = e4m3_encode2(div(to_f32<DT>(v[j] & 0xFFFFu)), div(to_f32<DT>(v[j] >> 16)));
+            u2 o = {c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
             __builtin_nontemporal_store(o, &qv[i]);
         }
         if (blockIdx.x == 0) {
@@ -152,22 +150,19 @@ __device__ __forceinline__ void cast_packed_tiles(const uint16_t* __restrict__ x
         u4 out[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            uint32_t c[16];
+            uint32_t c[8];  // code pairs
 #pragma unroll
-            for (int j = 0; j < 16; ++j) c[j] = 0;
+            for (int j = 0; j < 8; ++j) c[j] = 0;
             if (m < M && k + 16 * h < K) {
                 const u4* src = (const u4*)(x + m * K + k + 16 * h);
                 const u4 v0 = __builtin_nontemporal_load(src), v1 = __builtin_nontemporal_load(src + 1);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    c[2 * j] = e4m3_encode(div(to_f32<DT>(v0[j] & 0xFFFFu)));
-                    c[2 * j + 1] = e4m3_encode(div(to_f32<DT>(v0[j] >> 16)));
-                    c[8 + 2 * j] = e4m3_encode(div(to_f32<DT>(v1[j] & 0xFFFFu)));
-                    c[8 + 2 * j + 1] = e4m3_encode(div(to_f32<DT>(v1[j] >> 16)));
+                    c[j] = e4m3_encode2(div(to_f32<DT>(v0[j] & 0xFFFFu)), div(to_f32<DT>(v0[j] >> 16)));
+                    c[4 + j] = e4m3_encode2(div(to_f32<DT>(v1[j] & 0xFFFFu)), div(to_f32<DT>(v1[j] >> 16)));
                 }
             }
-            out[h] = u4{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
-                        pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15])};
+            out[h] = u4{c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
         }
         uint8_t* tile = xq + t * 2048 + lane * 16;
         *(u4*)tile = out[0];

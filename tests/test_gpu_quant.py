@@ -64,6 +64,24 @@ def test_exhaustive_patterns_static(dtype, scale):
     assert bad.size == 0, f"{bad.size} codes differ, e.g. bits {bits[bad[:4]]} got {got[bad[:4]]} want {q_ref.ravel()[bad[:4]]}"
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 0.0123])
+def test_static_nonfinite_inputs(dtype, scale):
+    """Every infinity and NaN pattern, plus signed zeros, with a caller's
+    scale: infinities saturate to the +-448 codes and NaNs give the NaN codes
+    with their sign kept, as the oracle encodes them."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    nonfinite = b[((b >> 10) & 31) == 31] if dtype == "f16" else b[((b >> 7) & 255) == 255]
+    bits = np.concatenate([nonfinite, np.array([0x0000, 0x8000], dtype=np.uint16)])
+    s = np.float32(scale)
+    xq = bql.quantize_static(dev16(bits, dtype), torch.tensor([s], device=DEV))
+    q_ref = oracle.quant_with_scales(oracle.decode_input(bits, dtype).reshape(1, -1), np.array([s])).ravel()
+    got = host(xq)
+    assert set(np.unique(q_ref).tolist()) == {0x00, 0x80, 0x7E, 0xFE, 0x7F, 0xFF}
+    bad = np.nonzero(got != q_ref)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, e.g. bits {bits[bad[:4]]} got {got[bad[:4]]} want {q_ref[bad[:4]]}"
+
+
 @pytest.mark.parametrize("M,K", [(16, 1024), (1, 4096), (16, 14336), (128, 4096), (1024, 14336),
                                  (1024, 4096)])
 def test_config_activations(M, K):
