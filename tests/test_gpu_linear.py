@@ -86,6 +86,30 @@ def test_cfg3_llama3_8b(idx, M):
     _fp8_case(3, idx, M, N, K, "bf16", False, "channels", torch.bfloat16)
 
 
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_small_m_two_strip_blocks_odd_count(M):
+    """N = 16400: 1025 channel strips, above the count where the small-M fp8
+    kernel gives each block two strips, so the last block has one; dynamic
+    quantization (fused for M <= 4), then pre-quantized A (row-major)."""
+    _fp8_case(3, 7, M, 16400, 256, "bf16", False, "channels", torch.bfloat16)
+    g = np.random.Generator(np.random.PCG64(54 + M))
+    N, K = 16400, 256
+    aq = _random_codes(g, (M, K))
+    wq = _random_codes(g, (N, K))
+    sa, sw = np.float32(0.5), np.float32(0.25)
+    pw = bql.prepack_weight(dev(wq), "fp8_tensor", scales=torch.tensor([sw], device=DEV))
+    y_ref = oracle.fp8_linear(aq, sa, wq, np.array([sw], dtype=np.float32))
+    for fast in (False, True):
+        y = bql.fp8_linear(dev(aq).view(torch.float8_e4m3fn), pw, a_scale=torch.tensor([sa], device=DEV),
+                           out_dtype=torch.float32, fast_accum=fast)
+        torch.cuda.synchronize()
+        if fast:
+            abs_sum = oracle.fp8_acc(aq & 0x7F, wq & 0x7F) * np.float64(sa) * np.float64(sw)
+            assert_fast_bound(host_f64(y), y_ref, abs_sum, f"pre-quantized M={M} N={N} fast")
+        else:
+            assert_close(host_f64(y), y_ref, f"pre-quantized M={M} N={N}")
+
+
 # -------------------------------------------------------------- config 4
 
 @pytest.mark.parametrize("idx", range(4))
