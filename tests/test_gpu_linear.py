@@ -206,6 +206,57 @@ def test_w4a8_ragged(M, N, K):
     assert np.array_equal(host(acc).astype(np.int64), oracle.w4a8_acc(aq, w))
 
 
+@pytest.mark.parametrize("M", [1, 3, 5, 16])
+def test_small_m_split_k(M):
+    """N = 256, K = 4096: the small-M kernels split K four ways (8 k-tiles
+    per split, so half of a wave's weight batches lie past its split's range)
+    and add the partial sums in a fixed order; fp8 (fused quantization for
+    M <= 4), W8A16 and W4A8."""
+    N, K = 256, 4096
+    _fp8_case(3, 12, M, N, K, "bf16", False, "channels", torch.bfloat16)
+    g = wl.rng(9, N, K, 12)
+    bits = wl.weight(g, N, K, "f16")
+    pw = bql.prepack_weight(dev16(bits, "f16"), "fp8_channel")
+    codes, s = oracle.quant_per_row(oracle.decode_input(bits, "f16"))
+    a_bits = wl.activation(wl.rng(9, M, 12), M, K, "f16")
+    y = bql.w8a16_linear(dev16(a_bits, "f16"), pw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_close(host_f64(y), oracle.w8a16_linear(oracle.decode_input(a_bits, "f16"), codes, s),
+                 f"W8A16 split K M={M}")
+    w = wl.int4_weight(g, N, K)
+    pw4 = bql.prepack_weight(dev(wl.pack_int4(w).reshape(N, K // 2)), "int4_channel",
+                             scales=dev16(wl.w4a8_channel_scales(g, N), "f16"))
+    aq = g.integers(-127, 128, (M, K), dtype=np.int8)
+    acc = bql.w4a8_linear(dev(aq), None, pw4, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc).astype(np.int64), oracle.w4a8_acc(aq, w))
+
+
+def test_w8a16_split_k_infinite_activation():
+    """M = 1, N = 256, K = 4096 (K split four ways); one activation column,
+    in the third split's range, is +inf.  Each output is then +-inf by the
+    sign of its weight code in that column, or NaN where that code is +-0,
+    as the oracle's IEEE sums give.  A split that read the column outside
+    its own range would multiply it by zero weight tiles and make every
+    output NaN."""
+    N, K = 256, 4096
+    g = np.random.Generator(np.random.PCG64(77))
+    wq = _random_codes(g, (N, K))
+    col = 2 * 1024 + 300
+    wq[0:3, col] = [0x00, 0x80, 0x38]
+    pw = bql.prepack_weight(dev(wq), "fp8_channel", scales=torch.ones(N, device=DEV))
+    a = oracle.decode_input(wl.activation(wl.rng(9, 1, 13), 1, K, "f16"), "f16").astype(np.float32)
+    a[0, col] = np.inf
+    y = bql.w8a16_linear(dev16(wl.to_bits(a, "f16"), "f16"), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = host_f64(y)[0]
+    with np.errstate(invalid="ignore"):
+        want = oracle.w8a16_linear(a, wq, np.ones(N, dtype=np.float32))[0]
+    assert np.isnan(want[:2]).all() and np.isposinf(want[2]) and not np.isfinite(want).any()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(want)], want[~np.isnan(want)])
+
+
 def test_w4a8_extreme_values_exact():
     # every product at its extreme: -127 * -8 * 16 per term, K = 8192
     N, K, M = 32, 8192, 17
