@@ -5,10 +5,12 @@
 // Two regimes, as the micro-benchmark on vLLM PR #4118 shows (small token
 // counts are a weight-streaming problem, large ones a matrix-core problem):
 //   * small M (<= 16 rows of A; W8A16 at every M): a streaming kernel.  Each
-//     wave walks k-tiles of a 16-channel weight strip, loading every MFMA
-//     operand straight from HBM with unconditional 16-byte buffer loads (the
-//     packed layout makes one wave-wide load 1 KiB contiguous; offsets past
-//     a descriptor's range read zeros).  A is read where it is: fp16
+//     wave walks k-tiles of a block's 16-channel weight strip (two strips
+//     per block when N is large), loading every MFMA operand straight from
+//     HBM with unconditional 16-byte buffer loads (the packed layout makes
+//     one wave-wide load 1 KiB contiguous; offsets past a descriptor's range
+//     read zeros) into two register sets used in turn, so that the next
+//     batch is in flight while one is multiplied.  A is read where it is: fp16
 //     row-major (W8A16), 8-bit row-major (pre-quantized fp8 / int8), or
 //     quantized by the kernel itself into LDS (fp8 with dynamic scaling,
 //     M <= 4).  Waves of a block split K and are summed through LDS in a
