@@ -77,10 +77,16 @@ def _declare(L):
     L.bqo_w8a16_linear.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
     L.bqo_w4a8_acc.argtypes = [_P, _P, _I64, _I64, _I64, _P, _I64, _P]
     L.bqo_w4a8_linear.argtypes = [_P, _P, _P, _I64, _P, _I64, _P]
+    L.bqo_rms_sumsq.restype = ctypes.c_double
+    L.bqo_rms_sumsq.argtypes = [_P, _I64]
+    L.bqo_rms_inv.restype = ctypes.c_float
+    L.bqo_rms_inv.argtypes = [ctypes.c_double, _I64, _F]
+    L.bqo_rmsnorm_apply.argtypes = [_P, _P, _P, _I64, _I64, _P]
+    L.bqo_rmsnorm.argtypes = [_P, _P, _I64, _I64, _F, _P, _P]
     for fn in ("bqo_decode_input", "bqo_quant_per_tensor", "bqo_quant_per_row",
                "bqo_quant_with_scales", "bqo_int8_quant_per_token", "bqo_unpack_int4",
                "bqo_fp8_acc", "bqo_fp8_linear", "bqo_fp8_output", "bqo_w8a16_linear",
-               "bqo_w4a8_acc", "bqo_w4a8_linear"):
+               "bqo_w4a8_acc", "bqo_w4a8_linear", "bqo_rmsnorm_apply", "bqo_rmsnorm"):
         getattr(L, fn).restype = None
 
 
@@ -254,6 +260,89 @@ def w4a8_linear(acc, sa, sw, rows=None) -> np.ndarray:
     y = np.empty((nr, N), dtype=np.float64)
     lib().bqo_w4a8_linear(_ptr(acc), _ptr(sa), _ptr(sw), N, _ptr(r), nr, _ptr(y))
     return y
+
+
+# ------------------------------------------------- RMSNorm ahead of quant
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float):
+    """RMSNorm in the precision the fused quantizers define (oracle.c):
+    returns (y float32 [M,K], r float32 [M])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32).ravel()
+    M, K = x.shape
+    assert g.size == K
+    y = np.empty((M, K), dtype=np.float32)
+    r = np.empty(M, dtype=np.float32)
+    lib().bqo_rmsnorm(_ptr(x), _ptr(g), M, K, float(eps), _ptr(y), _ptr(r))
+    return y, r
+
+
+def rmsnorm_apply(x: np.ndarray, g: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """y = fp32(fp32(x * r[m]) * g[k]) for given per-row r."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32).ravel()
+    r = np.ascontiguousarray(r, dtype=np.float32).ravel()
+    M, K = x.shape
+    assert g.size == K and r.size == M
+    y = np.empty((M, K), dtype=np.float32)
+    lib().bqo_rmsnorm_apply(_ptr(x), _ptr(g), _ptr(r), M, K, _ptr(y))
+    return y
+
+
+def rms_sumsq(x: np.ndarray) -> np.ndarray:
+    """Per-row fp64 sum of squares, in k order."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    L = lib()
+    return np.array([L.bqo_rms_sumsq(_ptr(x[m]), K) for m in range(M)], dtype=np.float64)
+
+
+def rms_inv(sumsq: float, K: int, eps: float) -> np.float32:
+    return np.float32(lib().bqo_rms_inv(float(sumsq), int(K), float(eps)))
+
+
+def rms_inv_candidates(x: np.ndarray, eps: float):
+    """Every fp32 r[m] the definition admits.
+
+    The definition sums the squares in fp64 without fixing the order, so a
+    sum taken in another order differs from the exact sum by at most
+    (K - 1) * 2^-53 of itself (all terms are non-negative).  The fp64 chain
+    that follows is monotone in the sum, so the admissible r are the fp32
+    values between the chain at the two ends of that interval (widened for
+    the oracle's own summation error and the chain's roundings).  Returns
+    (r_lo, r_hi) float32 [M]; they differ only for rows whose exact r lies
+    next to an fp32 rounding boundary, and then by one ulp."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    delta = (2.0 * K + 16.0) * 2.0 ** -53
+    ss = rms_sumsq(x)
+    lo = np.array([rms_inv(s * (1.0 + delta), K, eps) for s in ss], dtype=np.float32)
+    hi = np.array([rms_inv(s * (1.0 - delta), K, eps) for s in ss], dtype=np.float32)
+    assert np.all(lo <= hi)
+    assert np.all((hi == lo) | (hi == np.nextafter(lo, np.float32(np.inf)))), \
+        "more than two admissible r values"
+    return lo, hi
+
+
+def rmsnorm_int8_per_token(x: np.ndarray, g: np.ndarray, eps: float, r=None):
+    """RMSNorm then per-token int8: returns (codes int8, scales float32 [M], r).
+    r (optional) picks one admissible r per row (see rms_inv_candidates)."""
+    if r is None:
+        y, r = rmsnorm(x, g, eps)
+    else:
+        y = rmsnorm_apply(x, g, r)
+    q, s = int8_quant_per_token(y)
+    return q, s, r
+
+
+def rmsnorm_fp8_per_tensor(x: np.ndarray, g: np.ndarray, eps: float, r=None):
+    """RMSNorm then dynamic per-tensor E4M3: returns (codes uint8, scale, r)."""
+    if r is None:
+        y, r = rmsnorm(x, g, eps)
+    else:
+        y = rmsnorm_apply(x, g, r)
+    q, s = quant_per_tensor(y)
+    return q, s, r
 
 
 def within_tolerance(got: np.ndarray, ref: np.ndarray, rel: float = 5e-3, floor: float = 1e-2):

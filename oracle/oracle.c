@@ -304,3 +304,50 @@ void bqo_w4a8_linear(const int64_t* acc, const float* sa, const float* sw,
         for (int64_t n = 0; n < N; ++n)
             y[i * N + n] = (double)acc[i * N + n] * (double)sa[rows[i]] * (double)sw[n];
 }
+
+/* ------------------------------------------- RMSNorm ahead of quantization */
+
+/* The QQQ issue #15 answer on online activation quantization says the
+ * activation quantizer is fused into an element-wise kernel such as rmsnorm.
+ * The pages do not print RMSNorm itself; the standard root-mean-square
+ * normalization with eps inside the root is used:
+ *   r[m] = 1 / sqrt(mean_k x[m,k]^2 + eps),   y[m,k] = x[m,k] * r[m] * g[k].
+ * Precision (our reading, the pages give none): every square of a 16-bit
+ * input is exact in fp64 and the squares are summed in fp64; ms = sum / K,
+ * ms + eps, the square root and the reciprocal are fp64 operations, and r is
+ * that fp64 value rounded once to fp32; y = fp32(fp32(x * r) * g).  The
+ * quantizers above are then applied to y unchanged. */
+
+/* Sum of squares of one row, in fp64, in k order. */
+double bqo_rms_sumsq(const float* x, int64_t K) {
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) s += (double)x[k] * (double)x[k];
+    return s;
+}
+
+/* r = fp32(1 / sqrt(sumsq / K + eps)), each step an fp64 operation. */
+float bqo_rms_inv(double sumsq, int64_t K, float eps) {
+    double ms = sumsq / (double)K;
+    double d = ms + (double)eps;
+    double root = sqrt(d);
+    return (float)(1.0 / root);
+}
+
+/* y[m,k] = fp32(fp32(x[m,k] * r[m]) * g[k]) for given per-row r. */
+void bqo_rmsnorm_apply(const float* x, const float* g, const float* r, int64_t M,
+                       int64_t K, float* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            float t = x[m * K + k] * r[m];
+            y[m * K + k] = t * g[k];
+        }
+}
+
+/* Whole RMSNorm: r (fp32 [M]) from the rows, then y (fp32 [M,K]). */
+void bqo_rmsnorm(const float* x, const float* g, int64_t M, int64_t K, float eps,
+                 float* y, float* r) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) r[m] = bqo_rms_inv(bqo_rms_sumsq(x + m * K, K), K, eps);
+    bqo_rmsnorm_apply(x, g, r, M, K, y);
+}

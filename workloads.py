@@ -22,6 +22,8 @@ checkpoint or dataset is involved):
   cfg5  W4A8, K=N in {4096,5120,6656,8192}, M in {1,16,256,1024}: W int4
         ~U{-8..7}; A fp16 ~N(0,1) (quantized per token by each side); weight
         scales fp16 ~U[0.5,2] * 2^-8.
+  RMSNorm ahead of the quantizers: the activation recipe above as the
+        norm's input, gain g ~U[0.5, 1.5] in the activation dtype.
 """
 from __future__ import annotations
 
@@ -108,6 +110,12 @@ def int4_weight(g: np.random.Generator, N: int, K: int) -> np.ndarray:
 def w4a8_channel_scales(g: np.random.Generator, N: int) -> np.ndarray:
     s = g.uniform(0.5, 2.0, size=N).astype(np.float32) * np.float32(2.0 ** -8)
     return f32_to_f16_bits(s)
+
+
+def norm_weight(g: np.random.Generator, K: int, dtype: str) -> np.ndarray:
+    """RMSNorm gain g[k] ~ U[0.5, 1.5] as fp16/bf16 bits [K] (synthetic: the
+    pages give no trained values)."""
+    return to_bits(g.uniform(0.5, 1.5, size=K).astype(np.float32), dtype)
 
 
 def sample_rows(g: np.random.Generator, M: int, count: int) -> np.ndarray:
