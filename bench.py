@@ -349,6 +349,79 @@ def bench_w4a8(bql, dev, steps, warmup):
     return out
 
 
+def bench_rmsnorm_quant(bql, dev, steps, warmup):
+    """RMSNorm fused with the activation quantizers: per-token int8 at the
+    W4A8 activation shapes (M = 1024, K in {4096, 5120, 6656, 8192}, fp16)
+    and per-tensor E4M3 at the Llama hidden sizes (M = 1024, K = 4096 and
+    M = 4096, K = 8192, bf16 with outlier channels).  Inputs are rotated over
+    copies beyond twice the Infinity Cache.  GB/s of algorithmic bytes: x
+    read once, g, the codes and the scales written once."""
+    out = {"workload": "RMSNorm (gain U[0.5,1.5], eps 1e-5) fused with per-token int8 (W4A8 "
+                       "activations, fp16 N(0,1), M=1024, K in {4096,5120,6656,8192}) and with "
+                       "per-tensor E4M3 (bf16 N(0,1) with 1% outlier channels x20; M=1024 K=4096, "
+                       "M=4096 K=8192)"}
+
+    def inputs(M, K, dtype, outliers, idx):
+        g = wl.rng(98, idx, M, K)
+        xb = wl.activation(g, M, K, dtype, outliers)
+        gb = wl.norm_weight(g, K, dtype)
+        tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+        x = torch.from_numpy(xb.view(np.int16)).to(dev).view(tdt)
+        gw = torch.from_numpy(gb.view(np.int16)).to(dev).view(tdt)
+        copies = max(2, -(-ROTATE_BYTES // (2 * M * K)))
+        return [x.clone() for _ in range(copies)], gw
+
+    # per-token int8, the four W4A8 activation shapes as one step
+    M = 1024
+    xs, gs, qs, ss = [], [], [], []
+    for idx, K in enumerate(wl.CFG5_KN):
+        x, gw = inputs(M, K, "f16", "none", idx)
+        xs.append(x)
+        gs.append(gw)
+        qs.append(torch.empty((M, K), dtype=torch.int8, device=dev))
+        ss.append(torch.empty(M, dtype=torch.float32, device=dev))
+    L = bql.lib()
+
+    def step8(i):
+        for j, K in enumerate(wl.CFG5_KN):
+            x = xs[j][i % len(xs[j])]
+            bql._check("bql_rmsnorm_int8_quantize_per_token",
+                       L.bql_rmsnorm_int8_quantize_per_token(
+                           bql._ptr(x), bql._ptr(gs[j]), bql.F16, M, K, 1e-5, bql._ptr(qs[j]),
+                           bql._ptr(ss[j]), None, bql._stream(dev)))
+    nslots = max(len(x) for x in xs)
+    sec = timed_graphs(step8, nslots, steps, warmup, per_graph=SMALL_STEPS_PER_GRAPH)
+    byts = sum(2 * M * K + 2 * K + M * K + 4 * M for K in wl.CFG5_KN)
+    gbs = byts / sec / 1e9
+    out["int8_per_token_M1024"] = {
+        "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(sec * 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+    # per-tensor E4M3 (two launches: row statistics, then the cast)
+    for idx, (M, K) in enumerate([(1024, 4096), (4096, 8192)]):
+        x, gw = inputs(M, K, "bf16", "channels", 10 + idx)
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sc = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(256, L.bql_rmsnorm_quantize_workspace_size(M)), dtype=torch.uint8,
+                         device=dev)
+
+        def stepf(i, x=x, gw=gw, q=q, sc=sc, ws=ws, M=M, K=K):
+            xi = x[i % len(x)]
+            bql._check("bql_rmsnorm_fp8_quantize_dynamic",
+                       L.bql_rmsnorm_fp8_quantize_dynamic(
+                           bql._ptr(xi), bql._ptr(gw), bql.BF16, M, K, 1e-5, bql._ptr(q),
+                           bql._ptr(sc), None, bql._ptr(ws), ws.numel(), bql._stream(dev)))
+        sec = timed_graphs(stepf, len(x), steps, warmup, per_graph=SMALL_STEPS_PER_GRAPH)
+        byts = 2 * M * K + 2 * K + M * K + 4
+        gbs = byts / sec / 1e9
+        out[f"fp8_per_tensor_M{M}_K{K}"] = {
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(sec * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,6 +532,8 @@ def main():
     w8a16 = bench_w8a16(bql, dev, args.steps, args.warmup)
     log("timing W4A8 ...")
     w4a8 = bench_w4a8(bql, dev, args.steps, args.warmup)
+    log("timing RMSNorm + quantization ...")
+    norm_quant = bench_rmsnorm_quant(bql, dev, args.steps, args.warmup)
 
     out = {
         "metric": METRIC,
@@ -501,6 +576,7 @@ def main():
         "roofline": roof,
         "w8a16": w8a16,
         "w4a8": w4a8,
+        "rmsnorm_quant": norm_quant,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline ...")

@@ -11,6 +11,8 @@ Operations (see the header for the exact contracts):
   quantize_dynamic        per-tensor E4M3 with scale = amax / 448
   quantize_static         E4M3 with a given scale
   int8_quantize_per_token per-row int8 with scale = amax / 127
+  rmsnorm_int8_quantize_per_token   RMSNorm fused with per-row int8
+  rmsnorm_fp8_quantize_dynamic      RMSNorm fused with per-tensor E4M3
   prepack_weight          quantize + lay out a weight once after load
   unpack_weight           logical codes back from the packed layout
   fp8_linear              Y = (sA sW[n]) (Aq Wq^T), fp16/bf16/E4M3 output
@@ -59,6 +61,11 @@ SIGNATURES = {
     "bql_fp8_quantize_dynamic": (_I, [_P, _I, _I64, _P, _P, _P, _SZ, _P]),
     "bql_fp8_quantize_static": (_I, [_P, _I, _I64, _P, _P, _P]),
     "bql_int8_quantize_per_token": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
+    "bql_rmsnorm_quantize_workspace_size": (_SZ, [_I64]),
+    "bql_rmsnorm_int8_quantize_per_token": (_I, [_P, _P, _I, _I64, _I64, ctypes.c_float, _P, _P,
+                                                 _P, _P]),
+    "bql_rmsnorm_fp8_quantize_dynamic": (_I, [_P, _P, _I, _I64, _I64, ctypes.c_float, _P, _P, _P,
+                                              _P, _SZ, _P]),
     "bql_packed_weight_bytes": (_SZ, [_I64, _I64, _I]),
     "bql_prepack_workspace_size": (_SZ, [_I64, _I64, _I]),
     "bql_prepack_weight": (_I, [_P, _I, _I64, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P]),
@@ -157,6 +164,45 @@ def int8_quantize_per_token(x: torch.Tensor):
            lib().bql_int8_quantize_per_token(_ptr(x), _TORCH_TO_BQL[x.dtype], M, K, _ptr(xq),
                                              _ptr(sc), _stream(x.device)))
     return xq, sc
+
+
+def _rmsnorm_args(x: torch.Tensor, g: torch.Tensor):
+    _need_cuda(x, g)
+    if x.dim() != 2 or g.shape != (x.shape[1],) or g.dtype != x.dtype:
+        raise ValueError("x must be [M,K] and g [K] of the same dtype")
+    return x.shape
+
+
+def rmsnorm_int8_quantize_per_token(x: torch.Tensor, g: torch.Tensor, eps: float,
+                                    inv_rms: bool = False):
+    """RMSNorm(x) * g, then per-row int8: returns (codes int8 [M,K],
+    scales fp32 [M], inv_rms fp32 [M] or None)."""
+    M, K = _rmsnorm_args(x, g)
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    sc = torch.empty(M, dtype=torch.float32, device=x.device)
+    r = torch.empty(M, dtype=torch.float32, device=x.device) if inv_rms else None
+    _check("bql_rmsnorm_int8_quantize_per_token",
+           lib().bql_rmsnorm_int8_quantize_per_token(_ptr(x), _ptr(g), _TORCH_TO_BQL[x.dtype], M, K,
+                                                     float(eps), _ptr(xq), _ptr(sc), _ptr(r),
+                                                     _stream(x.device)))
+    return xq, sc, r
+
+
+def rmsnorm_fp8_quantize_dynamic(x: torch.Tensor, g: torch.Tensor, eps: float,
+                                 inv_rms: bool = False, ws: Optional[torch.Tensor] = None):
+    """RMSNorm(x) * g, then per-tensor E4M3: returns (codes uint8 [M,K],
+    scale fp32 [1], inv_rms fp32 [M] or None)."""
+    M, K = _rmsnorm_args(x, g)
+    L = lib()
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    r = torch.empty(M, dtype=torch.float32, device=x.device) if inv_rms else None
+    ws, nb = _workspace(L.bql_rmsnorm_quantize_workspace_size(M), x.device, ws)
+    _check("bql_rmsnorm_fp8_quantize_dynamic",
+           L.bql_rmsnorm_fp8_quantize_dynamic(_ptr(x), _ptr(g), _TORCH_TO_BQL[x.dtype], M, K,
+                                              float(eps), _ptr(xq), _ptr(scale), _ptr(r), _ptr(ws),
+                                              nb, _stream(x.device)))
+    return xq, scale, r
 
 
 # ------------------------------------------------------------------- weights

@@ -2,6 +2,7 @@
 // Nothing here allocates or synchronizes; see include/bql.h for the
 // contract of every entry point.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -129,6 +130,49 @@ bql_status bql_int8_quantize_per_token(const void* x, bql_dtype xdt, int64_t M, 
     CHECK(need_ptr(scales, "scales"));
     if (M == 0) return ok();
     return hip_status(bql::launch_int8_per_token(x, xdt, M, K, xq, scales, (hipStream_t)stream));
+}
+
+// ------------------------------------------------ RMSNorm + quantization
+
+size_t bql_rmsnorm_quantize_workspace_size(int64_t M) {
+    return M > 0 ? bql::rmsnorm_quant_ws_bytes(M) : 0;
+}
+
+static bql_status check_rmsnorm_args(const void* x, const void* g, bql_dtype xdt, int64_t M,
+                                     int64_t K, float eps, const void* xq, const float* inv_rms) {
+    if (!is_f16ish(xdt)) return fail(BQL_ERR_DTYPE, "x must be BQL_F16 or BQL_BF16");
+    CHECK(need_m(M));
+    if (K <= 0 || K % 16 || K > bql::RMSNORM_MAX_K)
+        return fail(BQL_ERR_SHAPE, "K=%lld must be a positive multiple of 16, at most %lld",
+                    (long long)K, (long long)bql::RMSNORM_MAX_K);
+    if (!(eps > 0.0f) || eps == INFINITY) return fail(BQL_ERR_ARG, "eps must be positive and finite");
+    CHECK(need_ptr(x, "x"));
+    CHECK(need_ptr(g, "g"));
+    CHECK(need_ptr(xq, "xq"));
+    if (inv_rms && (((uintptr_t)inv_rms) & 3u)) return fail(BQL_ERR_ALIGN, "inv_rms misaligned");
+    return BQL_OK;
+}
+
+bql_status bql_rmsnorm_int8_quantize_per_token(const void* x, const void* g, bql_dtype xdt,
+                                               int64_t M, int64_t K, float eps, int8_t* xq,
+                                               float* scales, float* inv_rms, bql_stream stream) {
+    CHECK(check_rmsnorm_args(x, g, xdt, M, K, eps, xq, inv_rms));
+    CHECK(need_scalar(scales, "scales"));
+    if (M == 0) return ok();
+    return hip_status(bql::launch_rmsnorm_int8(x, g, xdt, M, K, eps, xq, scales, inv_rms,
+                                               (hipStream_t)stream));
+}
+
+bql_status bql_rmsnorm_fp8_quantize_dynamic(const void* x, const void* g, bql_dtype xdt, int64_t M,
+                                            int64_t K, float eps, uint8_t* xq, float* scale_out,
+                                            float* inv_rms, void* ws, size_t ws_bytes,
+                                            bql_stream stream) {
+    CHECK(check_rmsnorm_args(x, g, xdt, M, K, eps, xq, inv_rms));
+    CHECK(need_scalar(scale_out, "scale_out"));
+    CHECK(need_ws(ws, ws_bytes, bql_rmsnorm_quantize_workspace_size(M)));
+    if (M == 0) return ok();
+    return hip_status(bql::launch_rmsnorm_fp8(x, g, xdt, M, K, eps, xq, scale_out, inv_rms, ws,
+                                              (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------- prepack

@@ -36,6 +36,18 @@ hipError_t launch_int8_per_token(const void* x, int xdt, int64_t M, int64_t K, i
 hipError_t launch_tensor_scale(const void* x, int xdt, int64_t numel, float qmax,
                                float* scale, void* ws, hipStream_t stream);
 
+// ----------------------------------------------------------- norm_quant.hip
+// RMSNorm fused with per-token int8 (one launch) or per-tensor E4M3 (two
+// launches; ws holds M row maxima and M inverse RMS values).  K <= 32768.
+constexpr int64_t RMSNORM_MAX_K = 32768;
+size_t rmsnorm_quant_ws_bytes(int64_t M);
+hipError_t launch_rmsnorm_int8(const void* x, const void* g, int xdt, int64_t M, int64_t K,
+                               float eps, int8_t* xq, float* scales, float* inv_rms,
+                               hipStream_t stream);
+hipError_t launch_rmsnorm_fp8(const void* x, const void* g, int xdt, int64_t M, int64_t K,
+                              float eps, uint8_t* xq, float* scale_out, float* inv_rms, void* ws,
+                              hipStream_t stream);
+
 // -------------------------------------------------------------- prepack.hip
 hipError_t launch_row_scales(const void* w, int wdt, int64_t N, int64_t K, float qmax,
                              float* scales, hipStream_t stream);

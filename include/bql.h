@@ -146,6 +146,48 @@ bql_status bql_int8_quantize_per_token(const void* x, bql_dtype xdt, int64_t M, 
                                        int8_t* xq, float* scales, bql_stream stream);
 
 /* ------------------------------------------------------------------------
+ * RMSNorm fused with activation quantization
+ *
+ * QQQ issue #15 (the answer on online activation quantization) fuses the
+ * activation quantizer into an element-wise kernel such as rmsnorm, so the
+ * normalized activation is never stored in 16 bits.  The pages do not print
+ * RMSNorm; it is the standard root-mean-square normalization with eps inside
+ * the root, computed in this precision:
+ *   r[m]   = fp32(1 / sqrt(sum_k x[m,k]^2 / K + eps)): the squares (exact)
+ *            are summed in fp64 in an unspecified order, the rest are fp64
+ *            operations, one rounding to fp32 at the end;
+ *   y[m,k] = fp32(fp32(x[m,k] * r[m]) * g[k]).
+ * y is then quantized exactly as the matching standalone quantizer quantizes
+ * its input.  Inputs must be finite.
+ *   x: [M,K] of dtype xdt (BQL_F16 or BQL_BF16); g: [K] of the same dtype.
+ *   K a multiple of 16, at most 32768 (else BQL_ERR_SHAPE).
+ *   eps: positive and finite (else BQL_ERR_ARG).
+ *   inv_rms: NULL, or [M] fp32 that receives r[m].
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes for bql_rmsnorm_fp8_quantize_dynamic over M rows. */
+size_t bql_rmsnorm_quantize_workspace_size(int64_t M);
+
+/* RMSNorm + per-token int8 (the W4A8 activations of QQQ issue #15):
+ *   scales[m] = fp32(max_k |y[m,k]| / 127)  (1.0 for an all-zero row),
+ *   xq[m,k] = clamp(round_half_even(fp32(y[m,k] / scales[m])), -127, 127).
+ * xq: [M,K] int8; scales: [M] fp32.  One launch, no workspace. */
+bql_status bql_rmsnorm_int8_quantize_per_token(const void* x, const void* g, bql_dtype xdt,
+                                               int64_t M, int64_t K, float eps, int8_t* xq,
+                                               float* scales, float* inv_rms, bql_stream stream);
+
+/* RMSNorm + dynamic per-tensor E4M3 (vLLM PR #4118, "Algorithm"):
+ *   scale = fp32(max_{m,k} |y[m,k]| / 448)  (1.0 when that is 0),
+ *   xq[m,k] = E4M3(fp32(y[m,k] / scale)), nearest even, saturating.
+ * xq: [M,K] E4M3 codes, row-major (bql_fp8_linear takes them with
+ * adt = BQL_E4M3 and a_scale = scale_out); scale_out: one fp32 (required).
+ * ws: >= bql_rmsnorm_quantize_workspace_size(M) bytes. */
+bql_status bql_rmsnorm_fp8_quantize_dynamic(const void* x, const void* g, bql_dtype xdt, int64_t M,
+                                            int64_t K, float eps, uint8_t* xq, float* scale_out,
+                                            float* inv_rms, void* ws, size_t ws_bytes,
+                                            bql_stream stream);
+
+/* ------------------------------------------------------------------------
  * Weight prepack (done once, after load)
  * ---------------------------------------------------------------------- */
 

@@ -120,6 +120,32 @@ def test_quantizer_validation(L):
     assert p(A16, 1, 0, 32, A16, A16, None) == OK
 
 
+def test_rmsnorm_quantizer_validation(L):
+    i8 = L.bql_rmsnorm_int8_quantize_per_token
+    f8 = L.bql_rmsnorm_fp8_quantize_dynamic
+    assert L.bql_rmsnorm_quantize_workspace_size(0) == 0
+    assert L.bql_rmsnorm_quantize_workspace_size(1024) >= 8 * 1024
+    assert L.bql_rmsnorm_quantize_workspace_size(1024) % 256 == 0
+    assert i8(A16, A16, 3, 4, 4096, 1e-5, A16, A16, None, None) == ERR_DTYPE
+    assert i8(A16, A16, 2, 4, 40, 1e-5, A16, A16, None, None) == ERR_SHAPE
+    assert i8(A16, A16, 2, 4, 32768 + 16, 1e-5, A16, A16, None, None) == ERR_SHAPE
+    assert i8(A16, A16, 2, 4, 4096, 0.0, A16, A16, None, None) == ERR_ARG
+    assert i8(A16, A16, 2, 4, 4096, float("nan"), A16, A16, None, None) == ERR_ARG
+    assert i8(A16, A16, 2, 4, 4096, float("inf"), A16, A16, None, None) == ERR_ARG
+    assert i8(A16, None, 2, 4, 4096, 1e-5, A16, A16, None, None) == ERR_NULL
+    assert i8(A16, MIS, 2, 4, 4096, 1e-5, A16, A16, None, None) == ERR_ALIGN
+    assert i8(A16, A16, 2, 4, 4096, 1e-5, A16, None, None, None) == ERR_NULL
+    assert i8(A16, A16, 2, 0, 4096, 1e-5, A16, A16, None, None) == OK
+    ws = L.bql_rmsnorm_quantize_workspace_size(4)
+    assert f8(A16, A16, 2, 4, 4096, 1e-5, A16, None, None, A16, ws, None) == ERR_NULL
+    assert f8(A16, A16, 2, 4, 4096, 1e-5, A16, A16, None, None, 0, None) == ERR_WS
+    assert f8(A16, A16, 2, 4, 4096, 1e-5, A16, A16, None, A16, ws - 1, None) == ERR_WS
+    assert f8(A16, A16, 2, 4, 4096, 1e-5, A16, A16, None, ctypes.c_void_p(0x10010), ws,
+              None) == ERR_ALIGN
+    assert f8(A16, A16, 2, 4, 4096, -1.0, A16, A16, None, A16, ws, None) == ERR_ARG
+    assert f8(A16, A16, 2, 0, 4096, 1e-5, A16, A16, None, None, 0, None) == OK
+
+
 def test_prepack_validation(L):
     f = L.bql_prepack_weight
     assert f(A16, 2, 64, 60, 1, None, 0, A16, A16, A16, 8192, None) == ERR_SHAPE
