@@ -12,27 +12,26 @@
 // The quantizers then act on y exactly as the standalone ones act on x:
 //   per-token int8 (QQQ issue #15):     s[m] = amax_m / 127, q = clamp(rne(y / s[m]), +-127);
 //   per-tensor E4M3 (vLLM PR #4118):    s = amax / 448,       q = E4M3(y / s);
-// with IEEE fp32 divisions (y is an arbitrary fp32 value here, so the
-// reciprocal shortcut of the 16-bit quantizers does not apply).
+// with IEEE fp32 divisions y / s, formed as described at quot_f32 below.
 //
-// Kernels.  A block owns a row and keeps it in registers (at most 4 chunks of
-// 8 elements per thread, so 256 threads cover K <= 8192 and 1024 threads
-// K <= 32768); the sum of squares and the row maximum are wave shuffles plus
-// a fixed-order fold over the block's waves.  Per-token int8 is one launch.
-// Per-tensor E4M3 has a grid-wide dependency (the amax of y over all rows),
-// so it is two launches: the row kernel stores r[m] and max_k |y[m,k]| in the
-// workspace, and every block of the cast kernel folds the M row maxima
-// itself before it re-reads its rows, recomputes y and writes the codes.  No
-// atomics, nothing to zero beforehand, and results do not depend on the
-// order in which blocks run.
+// Kernels.  Grids are persistent (at most 512 blocks of 256 threads, or 256
+// of 1024 threads for K > 8192); a block walks rows gridDim.x apart with
+// each row in registers (up to four 16-byte chunks of 8 elements per
+// thread), g held for all its rows, and the next row requested before the
+// current one is reduced and quantized.  The sum of squares and the row
+// maximum are wave shuffles plus a fixed-order fold over the block's waves.
+// Per-token int8 is one launch.  Per-tensor E4M3 has a grid-wide dependency
+// (the amax of y over all rows), so it is two launches: the row kernel
+// stores r[m] and the maximum of |y| over each block's rows in the
+// workspace, and every block of the cast kernel folds those (at most 512)
+// maxima itself before it re-reads its rows, recomputes y and writes the
+// codes.  No atomics, nothing to zero beforehand, and results do not depend
+// on the order in which blocks run.
 #include "device.h"
 #include "kernels.h"
 
 namespace bql {
 
-constexpr int NQ_CHUNKS = 4;        // 16-byte chunks per thread in the row kernel
-constexpr int NQ_CAST_T = 256;      // threads per block of the cast kernel
-constexpr int NQ_CAST_BLOCKS = 1024;
 
 // Sum over the block in a fixed order, returned to every thread.
 // `sh` holds >= 16 doubles.
@@ -62,126 +61,199 @@ __device__ __forceinline__ uint32_t pack4_i8(uint32_t c0, uint32_t c1, uint32_t 
     return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
-// MODE 0: RMSNorm + per-token int8, writes q8, scales and (optional) inv_rms.
-// MODE 1: first pass of RMSNorm + per-tensor E4M3: writes r_ws[m], the row
-//         maximum of |y| (as fp32 bits) to rowmax[m], and optional inv_rms.
-template <int DT, int BT, int MODE>
+// The IEEE fp32 quotient y / s of a finite y by a finite s > 0, from
+// inv = 1/s rounded to fp64 (one fp64 division per block): p = y * inv in
+// fp64 is within 2^-52 of y / s (relative).  The rounding boundaries of fp32
+// are the midpoints between neighbouring fp32 values; an exact quotient y / s
+// is never one of them in the normal range (a midpoint has a 25-bit odd
+// significand, and y = m * s would give y an odd part of at least 25 bits),
+// and when it is not, y - m*s is a non-zero multiple of 2^(e_m + e_s - 47),
+// which keeps y / s at least 2^-49 (relative) from every boundary.  So p
+// rounds to the same fp32 value as y / s.  Below the fp32 normal range both
+// are tiny values of the sign of y, whose quantization codes are zero either
+// way.  gfx950 runs fp64 multiplies and conversions at the fp32 rate: three
+// instructions instead of the IEEE division's eleven, one of which is a
+// quarter-rate reciprocal.
+__device__ __forceinline__ float quot_f32(float y, double inv) {
+    return (float)((double)y * inv);
+}
+
+// Two finite fp32 values -> E4M3 codes (first in bits 0-7): clamp to
+// [-448, 448] with med3 (signed zeros pass unchanged), then the nearest-even
+// conversion.  The inputs here are finite by contract, so the NaN handling
+// of the general encoder is not needed.
+__device__ __forceinline__ uint32_t e4m3_encode2_finite(float a, float b) {
+    const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+}
+
+__device__ __forceinline__ uint32_t int8_code(float q) {
+    float t = __builtin_rintf(q);  // ties to even
+    t = t > 127.0f ? 127.0f : (t < -127.0f ? -127.0f : t);
+    return (uint32_t)(int32_t)t & 0xFFu;
+}
+
+// Rows m = blockIdx.x, blockIdx.x + gridDim.x, ... of a block, each held as
+// CH 16-byte chunks per thread (chunk c = threadIdx.x + j * BT).  The next
+// row is requested before the current one is reduced and quantized, so its
+// HBM reads overlap the current row's arithmetic; g stays in registers.
+// MODE 0: RMSNorm + per-token int8: q8, scales and (optional) inv_rms.
+// MODE 1: first pass of RMSNorm + per-tensor E4M3: r_ws[m] (and inv_rms),
+//         and partial[blockIdx.x] = max |y| (fp32 bits) over the block's rows.
+template <int DT, int BT, int CH, int MODE>
 __global__ __launch_bounds__(BT) void rmsnorm_rows_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ g,
-                                                          int64_t K, float eps,
+                                                          int64_t M, int64_t K, float eps,
                                                           int8_t* __restrict__ q8,
                                                           float* __restrict__ scales,
                                                           float* __restrict__ inv_rms,
-                                                          uint32_t* __restrict__ rowmax,
+                                                          uint32_t* __restrict__ partial,
                                                           float* __restrict__ r_ws) {
     __shared__ double shd[16];
     __shared__ uint32_t shu[16];
-    const int64_t m = blockIdx.x;
     const int nch = (int)(K / 8);  // K is a multiple of 16
-    const u4* row = (const u4*)(x + m * K);
     const u4* gv = (const u4*)g;
-    u4 v[NQ_CHUNKS];
+    u4 w[CH], v[CH], nx[CH];
+    int64_t m = blockIdx.x;
 #pragma unroll
-    for (int j = 0; j < NQ_CHUNKS; ++j) {
+    for (int j = 0; j < CH; ++j) {
         const int c = threadIdx.x + j * BT;
+        const u4* row = (const u4*)(x + m * K);
         v[j] = c < nch ? __builtin_nontemporal_load(&row[c]) : u4{0u, 0u, 0u, 0u};
+        w[j] = c < nch ? gv[c] : u4{0u, 0u, 0u, 0u};
     }
-    double ss = 0.0;
+    uint32_t block_mb = 0;
+    for (; m < M; m += gridDim.x) {
+        const int64_t mn = m + gridDim.x;
+        const u4* nrow = (const u4*)(x + (mn < M ? mn : m) * K);
 #pragma unroll
-    for (int j = 0; j < NQ_CHUNKS; ++j) {
-        float f[8];
-        decode8<DT>(v[j], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += (double)f[e] * (double)f[e];  // exact squares
-    }
-    ss = block_sum_f64(ss, shd);
-    const double ms = ss / (double)K;
-    const double d = ms + (double)eps;
-    const float r = (float)(1.0 / __builtin_sqrt(d));
-
-    float y[NQ_CHUNKS][8];
-    uint32_t mb = 0;
-#pragma unroll
-    for (int j = 0; j < NQ_CHUNKS; ++j) {
-        const int c = threadIdx.x + j * BT;
-        const u4 w = c < nch ? gv[c] : u4{0u, 0u, 0u, 0u};
-        float f[8], gf[8];
-        decode8<DT>(v[j], f);
-        decode8<DT>(w, gf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float t = f[e] * r;
-            y[j][e] = t * gf[e];
-            const uint32_t a = __float_as_uint(y[j][e]) & 0x7FFFFFFFu;
-            mb = mb > a ? mb : a;
-        }
-    }
-    mb = block_max_u32(mb, shu);
-    if constexpr (MODE == 1) {
-        if (threadIdx.x == 0) {
-            rowmax[m] = mb;
-            r_ws[m] = r;
-            if (inv_rms) inv_rms[m] = r;
-        }
-    } else {
-        const float amax = __uint_as_float(mb);
-        const float s = amax == 0.0f ? 1.0f : amax / 127.0f;  // IEEE division
-        u2* out = (u2*)(q8 + m * K);
-#pragma unroll
-        for (int j = 0; j < NQ_CHUNKS; ++j) {
+        for (int j = 0; j < CH; ++j) {
             const int c = threadIdx.x + j * BT;
-            if (c < nch) {
-                uint32_t cc[8];
+            nx[j] = (mn < M && c < nch) ? __builtin_nontemporal_load(&nrow[c]) : u4{0u, 0u, 0u, 0u};
+        }
+        double ss = 0.0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float t = __builtin_rintf(y[j][e] / s);  // IEEE division, ties to even
-                    t = t > 127.0f ? 127.0f : (t < -127.0f ? -127.0f : t);
-                    cc[e] = (uint32_t)(int32_t)t & 0xFFu;
-                }
-                out[c] = u2{pack4_i8(cc[0], cc[1], cc[2], cc[3]), pack4_i8(cc[4], cc[5], cc[6], cc[7])};
+        for (int j = 0; j < CH; ++j) {
+            float f[8];
+            decode8<DT>(v[j], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += (double)f[e] * (double)f[e];  // exact squares
+        }
+        ss = block_sum_f64(ss, shd);
+        const double ms = ss / (double)K;
+        const double d = ms + (double)eps;
+        const float r = (float)(1.0 / __builtin_sqrt(d));
+
+        float y[CH][8];
+        uint32_t mb = 0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            float f[8], gf[8];
+            decode8<DT>(v[j], f);
+            decode8<DT>(w[j], gf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float t = f[e] * r;
+                y[j][e] = t * gf[e];
+                const uint32_t a = __float_as_uint(y[j][e]) & 0x7FFFFFFFu;
+                mb = mb > a ? mb : a;
             }
         }
-        if (threadIdx.x == 0) {
-            scales[m] = s;
-            if (inv_rms) inv_rms[m] = r;
+        if constexpr (MODE == 1) {
+            block_mb = block_mb > mb ? block_mb : mb;
+            if (threadIdx.x == 0) {
+                r_ws[m] = r;
+                if (inv_rms) inv_rms[m] = r;
+            }
+        } else {
+            mb = block_max_u32(mb, shu);
+            const float amax = __uint_as_float(mb);
+            const float s = amax == 0.0f ? 1.0f : amax / 127.0f;  // IEEE division
+            const double inv = 1.0 / (double)s;
+            u2* out = (u2*)(q8 + m * K);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int c = threadIdx.x + j * BT;
+                if (c < nch) {
+                    uint32_t cc[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) cc[e] = int8_code(quot_f32(y[j][e], inv));
+                    out[c] = u2{pack4_i8(cc[0], cc[1], cc[2], cc[3]),
+                                pack4_i8(cc[4], cc[5], cc[6], cc[7])};
+                }
+            }
+            if (threadIdx.x == 0) {
+                scales[m] = s;
+                if (inv_rms) inv_rms[m] = r;
+            }
         }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) v[j] = nx[j];
+    }
+    if constexpr (MODE == 1) {
+        block_mb = block_max_u32(block_mb, shu);
+        if (threadIdx.x == 0) partial[blockIdx.x] = block_mb;
     }
 }
 
-// Second pass of RMSNorm + per-tensor E4M3: fold the row maxima into the
-// scale, then rows [blockIdx.x * rpb, +rpb) are re-read and cast.
-template <int DT>
-__global__ __launch_bounds__(NQ_CAST_T) void rmsnorm_fp8_cast_kernel(
+// Second pass of RMSNorm + per-tensor E4M3: rows m = blockIdx.x,
+// + gridDim.x, ... are re-read and cast, each block first folding the
+// nparts block maxima of the first pass into the scale.  The first row is
+// requested before that fold and each next row before the current one is
+// cast.
+template <int DT, int BT, int CH>
+__global__ __launch_bounds__(BT) void rmsnorm_fp8_cast_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, int64_t M, int64_t K,
-    const uint32_t* __restrict__ rowmax, const float* __restrict__ r_ws, int64_t rpb,
+    const uint32_t* __restrict__ partial, int nparts, const float* __restrict__ r_ws,
     uint8_t* __restrict__ xq, float* __restrict__ scale_out) {
     __shared__ uint32_t shu[16];
+    const int nch = (int)(K / 8);
+    const u4* gv = (const u4*)g;
+    u4 w[CH], v[CH], nx[CH];
+    int64_t m = blockIdx.x;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = threadIdx.x + j * BT;
+        const u4* row = (const u4*)(x + m * K);
+        v[j] = c < nch ? __builtin_nontemporal_load(&row[c]) : u4{0u, 0u, 0u, 0u};
+        w[j] = c < nch ? gv[c] : u4{0u, 0u, 0u, 0u};
+    }
     uint32_t mb = 0;
-    for (int64_t i = threadIdx.x; i < M; i += NQ_CAST_T) mb = mb > rowmax[i] ? mb : rowmax[i];
+    for (int i = threadIdx.x; i < nparts; i += BT) mb = mb > partial[i] ? mb : partial[i];
     mb = block_max_u32(mb, shu);
     const float amax = __uint_as_float(mb);
     const float s = amax == 0.0f ? 1.0f : amax / 448.0f;  // IEEE division
+    const double inv = 1.0 / (double)s;
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-    const int nch = (int)(K / 8);
-    const u4* gv = (const u4*)g;
-    const int64_t m0 = (int64_t)blockIdx.x * rpb;
-    for (int64_t m = m0; m < m0 + rpb && m < M; ++m) {
-        const float r = r_ws[m];
-        const u4* row = (const u4*)(x + m * K);
-        u2* out = (u2*)(xq + m * K);
-        for (int c = threadIdx.x; c < nch; c += NQ_CAST_T) {
-            float f[8], gf[8];
-            decode8<DT>(__builtin_nontemporal_load(&row[c]), f);
-            decode8<DT>(gv[c], gf);
-            uint32_t pr[4];
+    for (; m < M; m += gridDim.x) {
+        const int64_t mn = m + gridDim.x;
+        const u4* nrow = (const u4*)(x + (mn < M ? mn : m) * K);
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float y0 = (f[e] * r) * gf[e];
-                const float y1 = (f[e + 1] * r) * gf[e + 1];
-                pr[e / 2] = e4m3_encode2(y0 / s, y1 / s);  // IEEE divisions
-            }
-            __builtin_nontemporal_store(u2{pr[0] | (pr[1] << 16), pr[2] | (pr[3] << 16)}, &out[c]);
+        for (int j = 0; j < CH; ++j) {
+            const int c = threadIdx.x + j * BT;
+            nx[j] = (mn < M && c < nch) ? __builtin_nontemporal_load(&nrow[c]) : u4{0u, 0u, 0u, 0u};
         }
+        const float r = r_ws[m];
+        u2* out = (u2*)(xq + m * K);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = threadIdx.x + j * BT;
+            if (c < nch) {
+                float f[8], gf[8], y[8];
+                decode8<DT>(v[j], f);
+                decode8<DT>(w[j], gf);
+                uint32_t pr[4];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = (f[e] * r) * gf[e];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2)
+                    pr[e / 2] = e4m3_encode2_finite(quot_f32(y[e], inv), quot_f32(y[e + 1], inv));
+                __builtin_nontemporal_store(u2{pr[0] | (pr[1] << 16), pr[2] | (pr[3] << 16)}, &out[c]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) v[j] = nx[j];
     }
 }
 
@@ -189,16 +261,38 @@ size_t rmsnorm_quant_ws_bytes(int64_t M) {
     return (size_t)(((8 * M) + 255) & ~int64_t(255));
 }
 
+// Threads per row and chunks per thread: 256 threads with 1, 2 or 4 chunks
+// up to K = 8192, then 1024 threads with 2 or 4 chunks up to K = 32768.
+// Grids are persistent: at most NQ_BLOCKS_256 (or NQ_BLOCKS_1024) blocks,
+// each walking rows gridDim.x apart.
+constexpr int64_t NQ_BLOCKS_256 = 512;
+constexpr int64_t NQ_BLOCKS_1024 = 256;
+
+static unsigned nq_grid(int64_t M, int BT) {
+    const int64_t cap = BT == 256 ? NQ_BLOCKS_256 : NQ_BLOCKS_1024;
+    return (unsigned)(M < cap ? M : cap);
+}
+
 template <int DT, int MODE>
-static void launch_rows(const void* x, const void* g, int64_t M, int64_t K, float eps, int8_t* q8,
-                        float* scales, float* inv_rms, uint32_t* rowmax, float* r_ws,
-                        hipStream_t stream) {
-    if (K <= 256 * NQ_CHUNKS * 8)
-        rmsnorm_rows_kernel<DT, 256, MODE><<<(unsigned)M, 256, 0, stream>>>(
-            (const uint16_t*)x, (const uint16_t*)g, K, eps, q8, scales, inv_rms, rowmax, r_ws);
-    else
-        rmsnorm_rows_kernel<DT, 1024, MODE><<<(unsigned)M, 1024, 0, stream>>>(
-            (const uint16_t*)x, (const uint16_t*)g, K, eps, q8, scales, inv_rms, rowmax, r_ws);
+static unsigned launch_rows(const void* x, const void* g, int64_t M, int64_t K, float eps,
+                            int8_t* q8, float* scales, float* inv_rms, uint32_t* partial,
+                            float* r_ws, hipStream_t stream) {
+    const uint16_t* xs = (const uint16_t*)x;
+    const uint16_t* gs = (const uint16_t*)g;
+#define NQ_ROWS(BT, CH)                                                                           \
+    do {                                                                                          \
+        const unsigned grid = nq_grid(M, BT);                                                     \
+        rmsnorm_rows_kernel<DT, BT, CH, MODE><<<grid, BT, 0, stream>>>(xs, gs, M, K, eps, q8,     \
+                                                                       scales, inv_rms, partial,  \
+                                                                       r_ws);                     \
+        return grid;                                                                              \
+    } while (0)
+    if (K <= 256 * 8) NQ_ROWS(256, 1);
+    if (K <= 256 * 16) NQ_ROWS(256, 2);
+    if (K <= 256 * 32) NQ_ROWS(256, 4);
+    if (K <= 1024 * 16) NQ_ROWS(1024, 2);
+    NQ_ROWS(1024, 4);
+#undef NQ_ROWS
 }
 
 hipError_t launch_rmsnorm_int8(const void* x, const void* g, int xdt, int64_t M, int64_t K,
@@ -211,23 +305,36 @@ hipError_t launch_rmsnorm_int8(const void* x, const void* g, int xdt, int64_t M,
     return hipGetLastError();
 }
 
+template <int DT>
+static void launch_fp8(const void* x, const void* g, int64_t M, int64_t K, float eps, uint8_t* xq,
+                       float* scale_out, float* inv_rms, void* ws, hipStream_t stream) {
+    uint32_t* partial = (uint32_t*)ws;
+    float* r_ws = (float*)((char*)ws + 4 * M);
+    const uint16_t* xs = (const uint16_t*)x;
+    const uint16_t* gs = (const uint16_t*)g;
+    const int nparts = (int)launch_rows<DT, 1>(x, g, M, K, eps, nullptr, nullptr, inv_rms, partial,
+                                               r_ws, stream);
+#define NQ_CAST(BT, CH)                                                                          \
+    do {                                                                                         \
+        rmsnorm_fp8_cast_kernel<DT, BT, CH><<<nq_grid(M, BT), BT, 0, stream>>>(                  \
+            xs, gs, M, K, partial, nparts, r_ws, xq, scale_out);                                 \
+        return;                                                                                  \
+    } while (0)
+    if (K <= 256 * 8) NQ_CAST(256, 1);
+    if (K <= 256 * 16) NQ_CAST(256, 2);
+    if (K <= 256 * 32) NQ_CAST(256, 4);
+    if (K <= 1024 * 16) NQ_CAST(1024, 2);
+    NQ_CAST(1024, 4);
+#undef NQ_CAST
+}
+
 hipError_t launch_rmsnorm_fp8(const void* x, const void* g, int xdt, int64_t M, int64_t K,
                               float eps, uint8_t* xq, float* scale_out, float* inv_rms, void* ws,
                               hipStream_t stream) {
-    uint32_t* rowmax = (uint32_t*)ws;
-    float* r_ws = (float*)((char*)ws + 4 * M);
-    const int64_t blocks = M < NQ_CAST_BLOCKS ? M : NQ_CAST_BLOCKS;
-    const int64_t rpb = (M + blocks - 1) / blocks;
-    const int64_t grid = (M + rpb - 1) / rpb;
-    if (xdt == IN_BF16) {
-        launch_rows<IN_BF16, 1>(x, g, M, K, eps, nullptr, nullptr, inv_rms, rowmax, r_ws, stream);
-        rmsnorm_fp8_cast_kernel<IN_BF16><<<(unsigned)grid, NQ_CAST_T, 0, stream>>>(
-            (const uint16_t*)x, (const uint16_t*)g, M, K, rowmax, r_ws, rpb, xq, scale_out);
-    } else {
-        launch_rows<IN_F16, 1>(x, g, M, K, eps, nullptr, nullptr, inv_rms, rowmax, r_ws, stream);
-        rmsnorm_fp8_cast_kernel<IN_F16><<<(unsigned)grid, NQ_CAST_T, 0, stream>>>(
-            (const uint16_t*)x, (const uint16_t*)g, M, K, rowmax, r_ws, rpb, xq, scale_out);
-    }
+    if (xdt == IN_BF16)
+        launch_fp8<IN_BF16>(x, g, M, K, eps, xq, scale_out, inv_rms, ws, stream);
+    else
+        launch_fp8<IN_F16>(x, g, M, K, eps, xq, scale_out, inv_rms, ws, stream);
     return hipGetLastError();
 }
 
