@@ -431,6 +431,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel launches (for a rocprofv3 run of that kernel)")
+    ap.add_argument("--rmsnorm-only", action="store_true",
+                    help="only the fused RMSNorm + quantization leg (for a rocprofv3 run of it)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc output folders")
     args = ap.parse_args()
@@ -446,6 +448,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bql.lib()
+    if args.rmsnorm_only:
+        print(json.dumps({"rmsnorm_quant": bench_rmsnorm_quant(bql, dev, args.steps, args.warmup)}),
+              flush=True)
+        return
 
     log("generating weights ...")
     host_w, rot = build_weights(bql, dev)
