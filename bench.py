@@ -457,7 +457,7 @@ def main():
     host_w, rot = build_weights(bql, dev)
     nrot = len(rot)
 
-    def run_pass(M, fast=False, prequant=False, timed=True):
+    def run_pass(M, fast=False, prequant=False, timed=True, static=False):
         abits, a = build_activations(M, dev)
         outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N, K in SHAPES]
         wss = [torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8,
@@ -466,11 +466,16 @@ def main():
         if prequant:
             pre = [bql.quantize_dynamic(x) for x in a]
             pre = [(q.view(torch.float8_e4m3fn), s) for q, s in pre]
+        if static:  # a calibrated input_scale per linear (here the tensor's own amax / 448)
+            st = [bql.quantize_dynamic(x)[1] for x in a]
 
         def step(i):
             ws_set = rot[i % nrot]
             for j in range(len(SHAPES)):
-                if prequant:
+                if static:
+                    bql.fp8_linear_static(a[j], ws_set[j], st[j], out_dtype=torch.bfloat16,
+                                          out=outs[j], ws=wss[j], fast_accum=fast)
+                elif prequant:
                     bql.fp8_linear(pre[j][0], ws_set[j], a_scale=pre[j][1], out_dtype=torch.bfloat16,
                                    out=outs[j], ws=wss[j], fast_accum=fast)
                 else:
@@ -529,6 +534,10 @@ def main():
     log("timing M=1024 fast ...")
     _, _, _, _, (sec_f, sec_f_eager), _, _ = run_pass(M, fast=True)
 
+    # static activation scale (checkpoint input_scale): no amax pass
+    log("timing M=1024 static scale ...")
+    _, _, _, _, (sec_s, _), _, _ = run_pass(M, static=True)
+
     # ---- M = 1 decode pass
     log("timing M=1 ...")
     _, _, _, _, (sec1, sec1_eager), flops1, byts1 = run_pass(1)
@@ -580,6 +589,11 @@ def main():
             "ms_per_step": round(sec_f * 1e3, 4), "roofline": roof_fast,
         },
         "roofline": roof,
+        "static_scale": {
+            "value": round(flops / sec_s / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(sec_s * 1e3, 4),
+            "note": "same M=1024 step with a given per-tensor activation scale "
+                    "(bql_fp8_linear_static: one cast launch per linear, no amax pass)"},
         "w8a16": w8a16,
         "w4a8": w4a8,
         "rmsnorm_quant": norm_quant,

@@ -16,6 +16,7 @@ Operations (see the header for the exact contracts):
   prepack_weight          quantize + lay out a weight once after load
   unpack_weight           logical codes back from the packed layout
   fp8_linear              Y = (sA sW[n]) (Aq Wq^T), fp16/bf16/E4M3 output
+  fp8_linear_static       the same with a given (static) activation scale
   w8a16_linear            Y = sW[n] (A Wq^T), fp16 activations
   w4a8_linear             int4 x int8 with int32 accumulation
 """
@@ -72,6 +73,8 @@ SIGNATURES = {
     "bql_unpack_weight": (_I, [_P, _I64, _I64, _I, _P, _P]),
     "bql_fp8_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "bql_fp8_linear": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ, _P]),
+    "bql_fp8_linear_static": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ,
+                                   _P]),
     "bql_w8a16_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "bql_w8a16_linear": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "bql_w4a8_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
@@ -290,6 +293,29 @@ def fp8_linear(a: torch.Tensor, pw: PackedWeight, a_scale: Optional[torch.Tensor
            L.bql_fp8_linear(_ptr(a), _TORCH_TO_BQL[a.dtype], _ptr(a_scale), _ptr(pw.packed),
                             _ptr(pw.scales), int(pw.per_channel), M, N, K, _ptr(output_scale),
                             _ptr(out), ydt, int(bool(fast_accum)), _ptr(ws), nb, _stream(a.device)))
+    return out
+
+
+def fp8_linear_static(a: torch.Tensor, pw: PackedWeight, a_scale: torch.Tensor,
+                      out_dtype: torch.dtype = torch.bfloat16,
+                      output_scale: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                      fast_accum: bool = False) -> torch.Tensor:
+    """Y = (sA sW[n]) (Aq Wq^T) with Aq = E4M3(A / a_scale) for a given fp32 [1]
+    activation scale (static input_scale, or one kept from an earlier call)."""
+    _need_cuda(a, a_scale, output_scale, out, ws)
+    L = lib()
+    M, K = a.shape
+    N = pw.N
+    ydt = _TORCH_TO_BQL[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.uint8 if ydt == E4M3 else out_dtype, device=a.device)
+    ws, nb = _workspace(L.bql_fp8_linear_workspace_size(M, N, K), a.device, ws)
+    _check("bql_fp8_linear_static",
+           L.bql_fp8_linear_static(_ptr(a), _TORCH_TO_BQL[a.dtype], _ptr(a_scale), _ptr(pw.packed),
+                                   _ptr(pw.scales), int(pw.per_channel), M, N, K,
+                                   _ptr(output_scale), _ptr(out), ydt, int(bool(fast_accum)),
+                                   _ptr(ws), nb, _stream(a.device)))
     return out
 
 

@@ -329,6 +329,59 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
 }
 
+bql_status bql_fp8_linear_static(const void* a, bql_dtype adt, const float* a_scale,
+                                 const void* w_packed, const float* w_scale, int w_per_channel,
+                                 int64_t M, int64_t N, int64_t K, const float* output_scale,
+                                 void* y, bql_dtype ydt, bql_accum accum, void* ws,
+                                 size_t ws_bytes, bql_stream stream) {
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(need_m(M));
+    CHECK(need_nk(N, K));
+    if (K > (int64_t(1) << 22)) return fail(BQL_ERR_SHAPE, "K above 2^22");
+    if (!is_f16ish(adt)) return fail(BQL_ERR_DTYPE, "A must be BQL_F16 or BQL_BF16");
+    if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_E4M3)
+        return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16, BQL_F32 or BQL_E4M3");
+    if (w_per_channel != 0 && w_per_channel != 1) return fail(BQL_ERR_ARG, "w_per_channel must be 0 or 1");
+    if (accum != BQL_ACCUM_EXACT && accum != BQL_ACCUM_FAST) return fail(BQL_ERR_ARG, "unknown accum %d", (int)accum);
+    if (M == 0) return ok();
+    CHECK(need_ptr(a, "a"));
+    CHECK(need_scalar(a_scale, "a_scale"));
+    CHECK(need_ptr(w_packed, "w_packed"));
+    CHECK(need_scalar(w_scale, "w_scale"));
+    CHECK(need_ptr(y, "y"));
+    if (ydt == BQL_E4M3) CHECK(need_scalar(output_scale, "output_scale"));
+    CHECK(need_ws(ws, ws_bytes, bql_fp8_linear_workspace_size(M, N, K)));
+
+    char* wsb = (char*)ws;
+    uint8_t* aq = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);
+    char* part = wsb + bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K));
+    const int variant = accum == BQL_ACCUM_FAST ? bql::V_FP8 : bql::V_FP8X;
+    bql::LinearArgs la;
+    la.variant = variant;
+    la.w = (const uint8_t*)w_packed;
+    la.M = M;
+    la.N = N;
+    la.K = K;
+    la.y = y;
+    la.ydt = ydt;
+    la.a_scale = a_scale;
+    la.w_scale = w_scale;
+    la.w_per_channel = w_per_channel;
+    la.out_scale = output_scale;
+    if (bql::fused_small_m(M, N, K)) {
+        // one launch: the small-M kernel casts A with the given scale itself
+        la.a = a;
+        la.fused = 1;
+        la.xdt = adt;
+        la.given_scale = a_scale;
+        return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+    }
+    hipError_t e = bql::launch_quant_static_packed(a, adt, M, K, a_scale, aq, s);
+    if (e != hipSuccess) return hip_status(e);
+    la.a = aq;
+    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+}
+
 size_t bql_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     return align256(bql::small_m_ws_bytes(M, N, K, bql::V_W8A16));

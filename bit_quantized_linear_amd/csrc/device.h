@@ -73,6 +73,23 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float y) {
     return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
 }
 
+// The IEEE fp32 quotient y / s of a finite fp32 y by a finite s > 0, from
+// inv = 1/s rounded to fp64 (one fp64 division, hoisted by the caller):
+// p = y * inv in fp64 is within 2^-52 of y / s (relative).  The rounding
+// boundaries of fp32 are the midpoints between neighbouring fp32 values; an
+// exact quotient y / s is never one of them in the normal range (a midpoint
+// has a 25-bit odd significand, and y = m * s would give y an odd part of at
+// least 25 bits), and when it is not, y - m*s is a non-zero multiple of
+// 2^(e_m + e_s - 47), which keeps y / s at least 2^-49 (relative) from every
+// boundary.  So p rounds to the same fp32 value as y / s.  Below the fp32
+// normal range both are tiny values of the sign of y, whose quantization
+// codes are zero either way.  gfx950 runs fp64 multiplies and conversions
+// at the fp32 rate: three instructions instead of the IEEE division's
+// eleven, one of which is a quarter-rate reciprocal.
+__device__ __forceinline__ float quot_f32(float y, double inv) {
+    return (float)((double)y * inv);
+}
+
 // fp32 -> OCP E4M3 code: round to nearest even on the bit pattern,
 // saturate magnitudes >= 448 to 0x7E, keep the sign (so -0 -> 0x80).
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {

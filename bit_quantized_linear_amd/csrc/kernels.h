@@ -29,6 +29,10 @@ hipError_t launch_pack_codes(const uint8_t* src, int64_t M, int64_t K, uint8_t* 
                              hipStream_t stream);
 hipError_t launch_quant_static(const void* x, int xdt, int64_t numel, const float* scale,
                                uint8_t* xq, hipStream_t stream);
+// E4M3 with a given scale of a row-major [M, K] activation, written in the
+// packed layout the linear kernels read.
+hipError_t launch_quant_static_packed(const void* x, int xdt, int64_t M, int64_t K,
+                                      const float* scale, uint8_t* xq, hipStream_t stream);
 hipError_t launch_int8_per_token(const void* x, int xdt, int64_t M, int64_t K, int8_t* xq,
                                  float* scales, hipStream_t stream);
 // amax over numel 16-bit values -> scale = amax / qmax (1 if amax == 0)
@@ -89,6 +93,8 @@ struct LinearArgs {
     float* scale_ws = nullptr;   // sA in the workspace (read by the split-K reduce)
     // small-M path only: 8-bit A is read row-major [M, K] (no repack launch)
     int a_rowmajor = 0;
+    // fused small-M fp8 with a static activation scale (no amax): sA = *given_scale
+    const float* given_scale = nullptr;
 };
 
 // Whether an fp8 call with dynamic quantization runs the fused small-M kernel.

@@ -48,6 +48,7 @@ struct LinParams {
     float* scale_out;       // fused quantization: optional copy of sA for the caller
     float* scale_ws;        // fused quantization: sA for the split-K reduce
     int a_rowmajor;         // small-M kernels: 8-bit A is row-major [M, K], not packed
+    const float* given_scale;  // fused quantization with a static scale (no amax) when set
 };
 
 template <int V> struct VT;
@@ -222,6 +223,7 @@ __device__ __forceinline__ int out_size(int ydt) {
 // reads all of A for the per-tensor amax (a max, so every block gets the
 // same scale bit for bit), then casts the A slice its K split needs into
 // LDS as [M][slice] codes.  One launch instead of amax, cast and GEMV.
+// With a static scale (p.given_scale) the amax is skipped.
 // Occupancy the small-M kernels are compiled for (waves per SIMD): enough
 // register room for two weight batches, A and the decoded operands without
 // spilling, and as many resident blocks as that leaves.
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
         __shared__ uint32_t sh[16];
         const uint16_t* x = (const uint16_t*)p.a;
         uint32_t mb = 0;
+        const bool given = p.given_scale != nullptr;  // uniform: a static scale, no amax
         auto fold = [&](const u4& v) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -305,15 +308,19 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
                 mb = mb > hi ? mb : hi;
             }
         };
+        if (given) {
+            sa = *p.given_scale;
+        } else {
 #pragma unroll
-        for (int h = 0; h < HOLD; ++h) fold(held[h]);
-        for (int64_t i = threadIdx.x + (int64_t)HOLD * T; i < nvec; i += T) fold(((const u4*)x)[i]);
-        mb = block_max_u32(mb, sh);
-        const float amax = p.xdt == IN_BF16 ? to_f32<IN_BF16>(mb) : to_f32<IN_F16>(mb);
-        sa = amax == 0.0f ? 1.0f : amax / 448.0f;  // IEEE division, as the standalone quantizer
-        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
-            if (p.scale_out) *p.scale_out = sa;
-            if (p.scale_ws) *p.scale_ws = sa;
+            for (int h = 0; h < HOLD; ++h) fold(held[h]);
+            for (int64_t i = threadIdx.x + (int64_t)HOLD * T; i < nvec; i += T) fold(((const u4*)x)[i]);
+            mb = block_max_u32(mb, sh);
+            const float amax = p.xdt == IN_BF16 ? to_f32<IN_BF16>(mb) : to_f32<IN_F16>(mb);
+            sa = amax == 0.0f ? 1.0f : amax / 448.0f;  // IEEE division, as the standalone quantizer
+            if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+                if (p.scale_out) *p.scale_out = sa;
+                if (p.scale_ws) *p.scale_ws = sa;
+            }
         }
         // x / sA as the standalone quantizer forms it: from the reciprocal
         // with one residual correction where that is the IEEE quotient's code
@@ -354,11 +361,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
                 }
             }
         };
-        const float y = 1.0f / sa;
-        if (recip_div_ok(sa))
-            cast_all([&](float v) { return div_by_scale(v, sa, y); });
-        else
-            cast_all([&](float v) { return v / sa; });
+        if (given) {
+            const double inv = 1.0 / (double)sa;
+            cast_all([&](float v) { return quot_f32(v, inv); });
+        } else {
+            const float y = 1.0f / sa;
+            if (recip_div_ok(sa))
+                cast_all([&](float v) { return div_by_scale(v, sa, y); });
+            else
+                cast_all([&](float v) { return v / sa; });
+        }
         __syncthreads();
     } else if constexpr (V == V_FP8 || V == V_FP8X) {
         sa = *p.ep.a_scale;
@@ -1226,13 +1238,15 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
     p.scale_out = args.scale_out;
     p.scale_ws = args.scale_ws;
     p.a_rowmajor = args.a_rowmajor;
+    p.given_scale = args.given_scale;
     if (use_small_m(args.variant, args.M, args.N, args.K)) {
         GemvPlan pl = plan_gemv(args.M, args.N, args.K);
         p.KT = pl.KT;
         p.kt_per_split = pl.kt_per_split;
         p.splits = pl.splits;
         if (args.fused) {
-            p.ep.a_scale = args.scale_ws;  // read by the split-K reduce
+            // read by the split-K reduce
+            p.ep.a_scale = args.given_scale ? args.given_scale : args.scale_ws;
             if (args.variant == V_FP8) return run_gemv<V_FP8, true>(p, stream);
             return run_gemv<V_FP8X, true>(p, stream);
         }

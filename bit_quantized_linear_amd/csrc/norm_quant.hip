@@ -12,7 +12,7 @@
 // The quantizers then act on y exactly as the standalone ones act on x:
 //   per-token int8 (QQQ issue #15):     s[m] = amax_m / 127, q = clamp(rne(y / s[m]), +-127);
 //   per-tensor E4M3 (vLLM PR #4118):    s = amax / 448,       q = E4M3(y / s);
-// with IEEE fp32 divisions y / s, formed as described at quot_f32 below.
+// with IEEE fp32 divisions y / s, formed as quot_f32 (device.h) forms them.
 //
 // Kernels.  Grids are persistent (at most 512 blocks of 256 threads, or 256
 // of 1024 threads for K > 8192); a block walks rows gridDim.x apart with
@@ -59,23 +59,6 @@ __device__ __forceinline__ void decode8(const u4& v, float* f) {
 
 __device__ __forceinline__ uint32_t pack4_i8(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
     return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-}
-
-// The IEEE fp32 quotient y / s of a finite y by a finite s > 0, from
-// inv = 1/s rounded to fp64 (one fp64 division per block): p = y * inv in
-// fp64 is within 2^-52 of y / s (relative).  The rounding boundaries of fp32
-// are the midpoints between neighbouring fp32 values; an exact quotient y / s
-// is never one of them in the normal range (a midpoint has a 25-bit odd
-// significand, and y = m * s would give y an odd part of at least 25 bits),
-// and when it is not, y - m*s is a non-zero multiple of 2^(e_m + e_s - 47),
-// which keeps y / s at least 2^-49 (relative) from every boundary.  So p
-// rounds to the same fp32 value as y / s.  Below the fp32 normal range both
-// are tiny values of the sign of y, whose quantization codes are zero either
-// way.  gfx950 runs fp64 multiplies and conversions at the fp32 rate: three
-// instructions instead of the IEEE division's eleven, one of which is a
-// quarter-rate reciprocal.
-__device__ __forceinline__ float quot_f32(float y, double inv) {
-    return (float)((double)y * inv);
 }
 
 // Two finite fp32 values -> E4M3 codes (first in bits 0-7): clamp to

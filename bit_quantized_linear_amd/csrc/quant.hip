@@ -200,6 +200,21 @@ __global__ __launch_bounds__(QT) void cast_e4m3_packed_kernel(const uint16_t* __
         cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, [&](float v) { return v / s; });
 }
 
+// Static-scale cast into the packed layout: s is given (checkpoint
+// input_scale, or a scale kept from an earlier call), so there is no amax
+// pass; x / s is the IEEE quotient formed by quot_f32.
+template <int DT>
+__global__ __launch_bounds__(QT) void cast_e4m3_packed_static_kernel(const uint16_t* __restrict__ x,
+                                                                     int64_t M, int64_t K, int64_t KT,
+                                                                     const float* __restrict__ given,
+                                                                     uint8_t* __restrict__ xq) {
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int64_t tiles = ((M + 15) / 16) * KT;
+    const double inv = 1.0 / (double)*given;
+    cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g,
+                          [&](float v) { return quot_f32(v, inv); });
+}
+
 // Row-major 8-bit codes [M, K] -> packed layout: one wave per 16 x 128
 // tile (grid-stride), lane l = r + 16 g moving row 16 mt + r, k = 128 kt +
 // 32 g .. +31 (two 16-byte loads) to tile + 16 l and tile + 1024 + 16 l, so
@@ -296,6 +311,20 @@ hipError_t launch_quant_static(const void* x, int xdt, int64_t numel, const floa
     else
         cast_e4m3_kernel<IN_F16, 1><<<cast_blocks(numel), QT, 0, stream>>>(
             (const uint16_t*)x, numel, nullptr, 0, scale, xq, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_static_packed(const void* x, int xdt, int64_t M, int64_t K,
+                                      const float* scale, uint8_t* xq, hipStream_t stream) {
+    const int64_t KT = (K + 127) / 128;
+    int64_t blocks = (((M + 15) / 16) * KT + QT / 64 - 1) / (QT / 64);
+    if (blocks > 8192) blocks = 8192;
+    if (xdt == IN_BF16)
+        cast_e4m3_packed_static_kernel<IN_BF16><<<(unsigned)blocks, QT, 0, stream>>>(
+            (const uint16_t*)x, M, K, KT, scale, xq);
+    else
+        cast_e4m3_packed_static_kernel<IN_F16><<<(unsigned)blocks, QT, 0, stream>>>(
+            (const uint16_t*)x, M, K, KT, scale, xq);
     return hipGetLastError();
 }
 

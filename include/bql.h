@@ -255,6 +255,21 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale,
                           void* y, bql_dtype ydt, bql_accum accum, void* ws, size_t ws_bytes,
                           bql_stream stream);
 
+/* FP8 linear with a static activation scale (vLLM discussion #5802 "RFC:
+ * FP8 Quantization Schema": per-tensor static scaling, the activation scale
+ * input_scale stored in the checkpoint; the same call serves a delayed scale
+ * kept from an earlier bql_fp8_linear call's a_scale output):
+ *   Aq = E4M3(fp32(A / a_scale)), nearest even, saturating (no amax pass),
+ *   Y[m,n] = (a_scale * sW[n]) * sum_k dec(Aq[m,k]) * dec(Wq[n,k]).
+ * a: [M,K] of adt = BQL_F16 or BQL_BF16.  a_scale: one positive finite fp32
+ * in device memory (input).  Every other argument, the output rules and the
+ * workspace size are those of bql_fp8_linear. */
+bql_status bql_fp8_linear_static(const void* a, bql_dtype adt, const float* a_scale,
+                                 const void* w_packed, const float* w_scale, int w_per_channel,
+                                 int64_t M, int64_t N, int64_t K, const float* output_scale,
+                                 void* y, bql_dtype ydt, bql_accum accum, void* ws,
+                                 size_t ws_bytes, bql_stream stream);
+
 /* Workspace bytes for bql_w8a16_linear at this shape. */
 size_t bql_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 

@@ -120,6 +120,23 @@ def test_quantizer_validation(L):
     assert p(A16, 1, 0, 32, A16, A16, None) == OK
 
 
+def test_fp8_linear_static_validation(L):
+    f = L.bql_fp8_linear_static
+    ws = L.bql_fp8_linear_workspace_size(4, 64, 64)
+
+    def call(a=A16, adt=2, sc=A16, w=A16, wsc=A16, pc=0, M=4, N=64, K=64, osc=None, y=A16, ydt=2,
+             acc=0, work=A16, wsb=ws):
+        return f(a, adt, sc, w, wsc, pc, M, N, K, osc, y, ydt, acc, work, wsb, None)
+    assert call(sc=None) == ERR_NULL
+    assert call(adt=4) == ERR_DTYPE          # pre-quantized input has no static cast
+    assert call(N=60) == ERR_SHAPE
+    assert call(ydt=4) == ERR_NULL           # fp8 out needs output_scale
+    assert call(acc=2) == ERR_ARG
+    assert call(work=None) == ERR_WS
+    assert call(sc=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    assert call(M=0, work=None, wsb=0) == OK
+
+
 def test_rmsnorm_quantizer_validation(L):
     i8 = L.bql_rmsnorm_int8_quantize_per_token
     f8 = L.bql_rmsnorm_fp8_quantize_dynamic
