@@ -349,6 +349,44 @@ def bench_w4a8(bql, dev, steps, warmup):
     return out
 
 
+def bench_small_n(bql, dev, steps, warmup):
+    """The MoE router shape (gate_proj with 8 experts) at N = 8 < 16: M = 4096
+    tokens, K = 4096, bf16 A with outlier channels, per-tensor weight, bf16
+    out.  A is rotated over copies beyond twice the Infinity Cache.  GB/s of
+    algorithmic bytes: end to end (dynamic quantization included: A read as
+    bf16) and the GEMM alone on pre-quantized E4M3 A."""
+    M, N, K = 4096, 8, 4096
+    g = wl.rng(96, 9)
+    wb = wl.weight(g, N, K, "bf16")
+    pw = bql.prepack_weight(torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16),
+                            "fp8_tensor")
+    a0 = torch.from_numpy(wl.activation(g, M, K, "bf16", "channels").view(np.int16)).to(dev)
+    copies = max(2, -(-ROTATE_BYTES // (2 * M * K)))
+    xs = [a0.view(torch.bfloat16).clone() for _ in range(copies)]
+    pre = [bql.quantize_dynamic(x) for x in xs]
+    pre = [(q.view(torch.float8_e4m3fn), sc) for q, sc in pre]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=dev)
+
+    def e2e(i):
+        bql.fp8_linear(xs[i % copies], pw, out_dtype=torch.bfloat16, out=y, ws=ws)
+
+    def gemm(i):
+        q, sc = pre[i % copies]
+        bql.fp8_linear(q, pw, a_scale=sc, out_dtype=torch.bfloat16, out=y, ws=ws)
+    out = {"workload": "MoE router fp8 linear at N = 8 experts (no padding of N in memory): "
+                       "M = 4096 tokens, K = 4096, bf16 A N(0,1) with 1% outlier channels x20, "
+                       "per-tensor E4M3 weight, bf16 out"}
+    for tag, fn, byts in (("end_to_end", e2e, 2 * M * K + N * K + 2 * M * N + 8),
+                          ("gemm_only", gemm, M * K + N * K + 2 * M * N + 8)):
+        sec = timed_graphs(fn, copies, steps, warmup, per_graph=SMALL_STEPS_PER_GRAPH)
+        gbs = byts / sec / 1e9
+        out[tag] = {"value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(sec * 1e6, 2),
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return out
+
+
 def bench_rmsnorm_quant(bql, dev, steps, warmup):
     """RMSNorm fused with the activation quantizers: per-token int8 at the
     W4A8 activation shapes (M = 1024, K in {4096, 5120, 6656, 8192}, fp16)
@@ -433,6 +471,8 @@ def main():
                     help="only the dominant-kernel launches (for a rocprofv3 run of that kernel)")
     ap.add_argument("--rmsnorm-only", action="store_true",
                     help="only the fused RMSNorm + quantization leg (for a rocprofv3 run of it)")
+    ap.add_argument("--small-n-only", action="store_true",
+                    help="only the small-N (MoE router) leg (for a rocprofv3 run of it)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc output folders")
     args = ap.parse_args()
@@ -451,6 +491,9 @@ def main():
     if args.rmsnorm_only:
         print(json.dumps({"rmsnorm_quant": bench_rmsnorm_quant(bql, dev, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.small_n_only:
+        print(json.dumps({"small_n": bench_small_n(bql, dev, args.steps, args.warmup)}), flush=True)
         return
 
     log("generating weights ...")
@@ -549,6 +592,8 @@ def main():
     w4a8 = bench_w4a8(bql, dev, args.steps, args.warmup)
     log("timing RMSNorm + quantization ...")
     norm_quant = bench_rmsnorm_quant(bql, dev, args.steps, args.warmup)
+    log("timing small N ...")
+    small_n = bench_small_n(bql, dev, args.steps, args.warmup)
 
     out = {
         "metric": METRIC,
@@ -597,6 +642,7 @@ def main():
         "w8a16": w8a16,
         "w4a8": w4a8,
         "rmsnorm_quant": norm_quant,
+        "small_n": small_n,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline ...")

@@ -8,6 +8,7 @@
 
 #include "bql.h"
 #include "kernels.h"
+#include "skinny.h"
 
 namespace {
 
@@ -53,6 +54,17 @@ bql_status need_nk(int64_t N, int64_t K) {
         return fail(BQL_ERR_SHAPE, "N=%lld and K=%lld must be multiples of 16", (long long)N, (long long)K);
     if (N > MAX_DIM || K > MAX_DIM) return fail(BQL_ERR_SHAPE, "N or K above 2^24");
     return BQL_OK;
+}
+
+// The fp8 formats also take 1 <= N < 16 (the small-N path); K stays a
+// multiple of 16.
+bql_status need_nk_fp8(int64_t N, int64_t K) {
+    if (N >= 1 && N < 16) {
+        if (K <= 0 || K % 16 || K > MAX_DIM)
+            return fail(BQL_ERR_SHAPE, "K=%lld must be a positive multiple of 16", (long long)K);
+        return BQL_OK;
+    }
+    return need_nk(N, K);
 }
 
 bql_status need_m(int64_t M) {
@@ -192,7 +204,7 @@ bql_status bql_prepack_weight(const void* w, bql_dtype wdt, int64_t N, int64_t K
                               const void* scales_in, bql_dtype sdt, void* packed,
                               float* scales_out, void* ws, size_t ws_bytes, bql_stream stream) {
     hipStream_t s = (hipStream_t)stream;
-    CHECK(need_nk(N, K));
+    CHECK(fmt == BQL_WFMT_INT4_CHANNEL ? need_nk(N, K) : need_nk_fp8(N, K));
     CHECK(need_ptr(w, "w"));
     CHECK(need_ptr(packed, "packed"));
     CHECK(need_ptr(scales_out, "scales_out"));
@@ -233,7 +245,7 @@ bql_status bql_prepack_weight(const void* w, bql_dtype wdt, int64_t N, int64_t K
 
 bql_status bql_unpack_weight(const void* packed, int64_t N, int64_t K, bql_wfmt fmt, void* out,
                              bql_stream stream) {
-    CHECK(need_nk(N, K));
+    CHECK(fmt == BQL_WFMT_INT4_CHANNEL ? need_nk(N, K) : need_nk_fp8(N, K));
     CHECK(need_ptr(packed, "packed"));
     CHECK(need_ptr(out, "out"));
     if (fmt == BQL_WFMT_INT4_CHANNEL)
@@ -253,13 +265,42 @@ size_t bql_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
            align256(bql::small_m_ws_bytes(M, N, K, bql::V_FP8));
 }
 
+// N < 16: the small-N kernel reads A where it is (E4M3 codes, or fp16 /
+// bf16 cast in registers with the given scale or with amax / 448 from the
+// amax partials of one pass over A, kept in the workspace).
+static bql_status skinny_fp8_linear(const void* a, bql_dtype adt, const float* a_scale,
+                                    float* scale_out, bool static_scale, const void* w_packed,
+                                    const float* w_scale, int w_per_channel, int64_t M, int64_t N,
+                                    int64_t K, const float* output_scale, void* y, bql_dtype ydt,
+                                    bql_accum accum, void* ws, hipStream_t s) {
+    int nparts = 0;
+    uint32_t* partial = (uint32_t*)ws;
+    if (adt != BQL_E4M3 && !static_scale) {
+        nparts = bql::launch_amax_partials(a, M * K, partial, s);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_status(e);
+    }
+    bql::Epilogue ep;
+    ep.y = y;
+    ep.ldy = N;
+    ep.ydt = ydt;
+    ep.a_scale = a_scale;
+    ep.w_scale = w_scale;
+    ep.w_per_channel = w_per_channel;
+    ep.out_scale = output_scale;
+    const int src = adt == BQL_E4M3 ? 4 : (adt == BQL_BF16 ? 2 : 1);
+    return hip_status(bql::launch_skinny_linear(a, src, (const uint8_t*)w_packed, M, N, K, a_scale,
+                                                partial, nparts, scale_out, ep,
+                                                accum == BQL_ACCUM_FAST, s));
+}
+
 bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const void* w_packed,
                           const float* w_scale, int w_per_channel, int64_t M, int64_t N, int64_t K,
                           const float* output_scale, void* y, bql_dtype ydt, bql_accum accum,
                           void* ws, size_t ws_bytes, bql_stream stream) {
     hipStream_t s = (hipStream_t)stream;
     CHECK(need_m(M));
-    CHECK(need_nk(N, K));
+    CHECK(need_nk_fp8(N, K));
     if (K > (int64_t(1) << 22)) return fail(BQL_ERR_SHAPE, "K above 2^22");
     if (!is_f16ish(adt) && adt != BQL_E4M3) return fail(BQL_ERR_DTYPE, "A must be BQL_F16, BQL_BF16 or BQL_E4M3");
     if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_E4M3)
@@ -276,6 +317,9 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     if (ydt == BQL_E4M3) CHECK(need_scalar(output_scale, "output_scale"));
     CHECK(need_ws(ws, ws_bytes, bql_fp8_linear_workspace_size(M, N, K)));
 
+    if (N <= bql::SKINNY_MAX_N)
+        return skinny_fp8_linear(a, adt, a_scale, a_scale, false, w_packed, w_scale, w_per_channel,
+                                 M, N, K, output_scale, y, ydt, accum, ws, s);
     char* wsb = (char*)ws;
     uint8_t* aq = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);
     char* part = wsb + bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K));
@@ -336,7 +380,7 @@ bql_status bql_fp8_linear_static(const void* a, bql_dtype adt, const float* a_sc
                                  size_t ws_bytes, bql_stream stream) {
     hipStream_t s = (hipStream_t)stream;
     CHECK(need_m(M));
-    CHECK(need_nk(N, K));
+    CHECK(need_nk_fp8(N, K));
     if (K > (int64_t(1) << 22)) return fail(BQL_ERR_SHAPE, "K above 2^22");
     if (!is_f16ish(adt)) return fail(BQL_ERR_DTYPE, "A must be BQL_F16 or BQL_BF16");
     if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_E4M3)
@@ -351,6 +395,9 @@ bql_status bql_fp8_linear_static(const void* a, bql_dtype adt, const float* a_sc
     CHECK(need_ptr(y, "y"));
     if (ydt == BQL_E4M3) CHECK(need_scalar(output_scale, "output_scale"));
     CHECK(need_ws(ws, ws_bytes, bql_fp8_linear_workspace_size(M, N, K)));
+    if (N <= bql::SKINNY_MAX_N)
+        return skinny_fp8_linear(a, adt, a_scale, nullptr, true, w_packed, w_scale, w_per_channel,
+                                 M, N, K, output_scale, y, ydt, accum, ws, s);
 
     char* wsb = (char*)ws;
     uint8_t* aq = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(PT) void prepack_fp8_kernel(const void* __restrict_
                                                          const float* __restrict__ scales,
                                                          int per_row, uint8_t* __restrict__ packed) {
     const int64_t q = (int64_t)blockIdx.x * PT + threadIdx.x;
-    const int64_t total = (N / TILE_N) * KT * (FP8_TILE_BYTES / 16);
+    const int64_t total = ((N + TILE_N - 1) / TILE_N) * KT * (FP8_TILE_BYTES / 16);
     if (q >= total) return;
     const int64_t tile = q / (FP8_TILE_BYTES / 16);
     const int c = (int)(q % (FP8_TILE_BYTES / 16));
@@ -60,7 +60,9 @@ __global__ __launch_bounds__(PT) void prepack_fp8_kernel(const void* __restrict_
     const int64_t n = nt * TILE_N + (lane & 15);
     const int64_t k0 = kt * TILE_K + 32 * (lane >> 4) + 16 * h;
     uint32_t out[4] = {0, 0, 0, 0};
-    if (k0 < K) {  // K is a multiple of 16: the chunk is whole or absent
+    // K is a multiple of 16: the chunk is whole or absent; channels past N
+    // (only when N < 16) are zero codes
+    if (k0 < K && n < N) {
         if constexpr (SRC == 4) {
             const uint32_t* src = (const uint32_t*)((const uint8_t*)w + n * K + k0);
 #pragma unroll
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(PT) void unpack_fp8_kernel(const uint8_t* __restric
                                                         int64_t N, int64_t K, int64_t KT,
                                                         uint8_t* __restrict__ out) {
     const int64_t q = (int64_t)blockIdx.x * PT + threadIdx.x;
-    const int64_t total = (N / TILE_N) * KT * (FP8_TILE_BYTES / 16);
+    const int64_t total = ((N + TILE_N - 1) / TILE_N) * KT * (FP8_TILE_BYTES / 16);
     if (q >= total) return;
     const int64_t tile = q / (FP8_TILE_BYTES / 16);
     const int c = (int)(q % (FP8_TILE_BYTES / 16));
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(PT) void unpack_fp8_kernel(const uint8_t* __restric
     const int64_t nt = tile / KT, kt = tile % KT;
     const int64_t n = nt * TILE_N + (lane & 15);
     const int64_t k0 = kt * TILE_K + 32 * (lane >> 4) + 16 * h;
-    if (k0 >= K) return;
+    if (k0 >= K || n >= N) return;
     const u4 v = *(const u4*)(packed + tile * FP8_TILE_BYTES + h * 1024 + lane * 16);
     uint32_t* dst = (uint32_t*)(out + n * K + k0);
 #pragma unroll
@@ -168,7 +170,7 @@ hipError_t launch_convert_scales(const void* s, int sdt, int64_t count, float* o
 hipError_t launch_prepack_fp8(const void* w, int wdt, int64_t N, int64_t K, const float* scales,
                               int per_row, uint8_t* packed, hipStream_t stream) {
     const int64_t KT = (K + TILE_K - 1) / TILE_K;
-    const unsigned nb = blocks_for((N / TILE_N) * KT * (FP8_TILE_BYTES / 16));
+    const unsigned nb = blocks_for(((N + TILE_N - 1) / TILE_N) * KT * (FP8_TILE_BYTES / 16));
     if (wdt == IN_F16)
         prepack_fp8_kernel<IN_F16><<<nb, PT, 0, stream>>>(w, N, K, KT, scales, per_row, packed);
     else if (wdt == IN_BF16)
@@ -188,7 +190,7 @@ hipError_t launch_prepack_int4(const uint8_t* w, int64_t N, int64_t K, uint8_t* 
 hipError_t launch_unpack_fp8(const uint8_t* packed, int64_t N, int64_t K, uint8_t* out,
                              hipStream_t stream) {
     const int64_t KT = (K + TILE_K - 1) / TILE_K;
-    unpack_fp8_kernel<<<blocks_for((N / TILE_N) * KT * (FP8_TILE_BYTES / 16)), PT, 0, stream>>>(
+    unpack_fp8_kernel<<<blocks_for(((N + TILE_N - 1) / TILE_N) * KT * (FP8_TILE_BYTES / 16)), PT, 0, stream>>>(
         packed, N, K, KT, out);
     return hipGetLastError();
 }

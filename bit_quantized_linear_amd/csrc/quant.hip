@@ -12,6 +12,7 @@
 // online activation quantization): one block per row.
 #include "device.h"
 #include "kernels.h"
+#include "skinny.h"
 
 namespace bql {
 
@@ -326,6 +327,12 @@ hipError_t launch_quant_static_packed(const void* x, int xdt, int64_t M, int64_t
         cast_e4m3_packed_static_kernel<IN_F16><<<(unsigned)blocks, QT, 0, stream>>>(
             (const uint16_t*)x, M, K, KT, scale, xq);
     return hipGetLastError();
+}
+
+int launch_amax_partials(const void* x, int64_t numel, uint32_t* partial, hipStream_t stream) {
+    const int nb = amax_blocks(numel);
+    amax_partial_kernel<<<nb, QT, 0, stream>>>((const uint16_t*)x, numel, partial);
+    return nb;
 }
 
 hipError_t launch_tensor_scale(const void* x, int xdt, int64_t numel, float qmax,

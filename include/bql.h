@@ -31,7 +31,10 @@
  *     unpacked weight is [N,K] (the nn.Linear layout, Y = A . W^T).  No bias.
  *   - N and K must be multiples of 16 (the FP8 GEMMs on the pages need
  *     dimensions divisible by 16; vLLM discussion #5802, the gate_proj
- *     question), else BQL_ERR_SHAPE.  M >= 0 is free; M = 0 is a no-op.
+ *     question), else BQL_ERR_SHAPE.  The fp8 formats (prepack, unpack,
+ *     bql_fp8_linear, bql_fp8_linear_static) also take 1 <= N <= 15, the
+ *     MoE router of that question (8 experts), without padding N in any
+ *     caller-visible buffer.  M >= 0 is free; M = 0 is a no-op.
  *   - Device pointers must be 16-byte aligned, else BQL_ERR_ALIGN.  With
  *     M = 0 the activation, weight and output pointers are not examined.
  *   - Arguments are checked on the host before anything is enqueued; on an

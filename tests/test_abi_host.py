@@ -120,6 +120,24 @@ def test_quantizer_validation(L):
     assert p(A16, 1, 0, 32, A16, A16, None) == OK
 
 
+def test_small_n_shape_rule(L):
+    # the fp8 formats take 1 <= N <= 15 (one padded strip); others keep N % 16
+    assert L.bql_packed_weight_bytes(8, 4096, 1) == 32 * 2048
+    assert L.bql_packed_weight_bytes(1, 48, 2) == 2048
+    f = L.bql_fp8_linear
+    for N, want in ((8, OK), (1, OK), (15, OK), (24, ERR_SHAPE), (0, ERR_SHAPE)):
+        assert f(A16, 2, None, A16, A16, 0, 0, N, 64, None, A16, 2, 0, None, 0, None) == want, N
+    assert f(A16, 2, None, A16, A16, 0, 0, 8, 40, None, A16, 2, 0, None, 0, None) == ERR_SHAPE
+    s = L.bql_fp8_linear_static
+    assert s(A16, 2, A16, A16, A16, 0, 0, 8, 64, None, A16, 2, 0, None, 0, None) == OK
+    w = L.bql_w8a16_linear
+    assert w(A16, A16, A16, 0, 8, 64, A16, 1, None, 0, None) == ERR_SHAPE
+    q = L.bql_w4a8_linear
+    assert q(A16, A16, A16, A16, 0, 8, 64, A16, 1, None, 0, None) == ERR_SHAPE
+    p = L.bql_prepack_weight
+    assert p(A16, 7, 8, 64, 3, A16, 1, A16, A16, None, 0, None) == ERR_SHAPE  # int4 keeps N % 16
+
+
 def test_fp8_linear_static_validation(L):
     f = L.bql_fp8_linear_static
     ws = L.bql_fp8_linear_workspace_size(4, 64, 64)
