@@ -77,6 +77,7 @@ def _declare(L):
     L.bqo_w8a16_linear.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
     L.bqo_w4a8_acc.argtypes = [_P, _P, _I64, _I64, _I64, _P, _I64, _P]
     L.bqo_w4a8_linear.argtypes = [_P, _P, _P, _I64, _P, _I64, _P]
+    L.bqo_w4a8_group_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P]
     L.bqo_rms_sumsq.restype = ctypes.c_double
     L.bqo_rms_sumsq.argtypes = [_P, _I64]
     L.bqo_rms_inv.restype = ctypes.c_float
@@ -86,7 +87,8 @@ def _declare(L):
     for fn in ("bqo_decode_input", "bqo_quant_per_tensor", "bqo_quant_per_row",
                "bqo_quant_with_scales", "bqo_int8_quant_per_token", "bqo_unpack_int4",
                "bqo_fp8_acc", "bqo_fp8_linear", "bqo_fp8_output", "bqo_w8a16_linear",
-               "bqo_w4a8_acc", "bqo_w4a8_linear", "bqo_rmsnorm_apply", "bqo_rmsnorm"):
+               "bqo_w4a8_acc", "bqo_w4a8_linear", "bqo_rmsnorm_apply", "bqo_rmsnorm",
+               "bqo_w4a8_group_linear"):
         getattr(L, fn).restype = None
 
 
@@ -343,6 +345,24 @@ def rmsnorm_fp8_per_tensor(x: np.ndarray, g: np.ndarray, eps: float, r=None):
         y = rmsnorm_apply(x, g, r)
     q, s = quant_per_tensor(y)
     return q, s, r
+
+
+def w4a8_group_linear(aq, sa, w4, sw, group=128, rows=None) -> np.ndarray:
+    """Per-group W4A8 (QQQ issue #15 "qqq-g128", read as one scale per
+    output channel and 128-k group): Y = sA[m] * sum_g sW[n,g] * acc_g[m,n],
+    acc_g the exact integer sum over group g; fp64.  sw: [N, G]."""
+    aq = np.ascontiguousarray(aq, dtype=np.int8)
+    w4 = np.ascontiguousarray(w4, dtype=np.int8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32).ravel()
+    M, K = aq.shape
+    N = w4.shape[0]
+    G = (K + group - 1) // group
+    sw = np.ascontiguousarray(sw, dtype=np.float32).reshape(N, G)
+    r = _rows(rows, M)
+    y = np.empty((r.size, N), dtype=np.float64)
+    lib().bqo_w4a8_group_linear(_ptr(aq), _ptr(sa), _ptr(w4), _ptr(sw), M, N, K, group, _ptr(r),
+                                r.size, _ptr(y))
+    return y
 
 
 def within_tolerance(got: np.ndarray, ref: np.ndarray, rel: float = 5e-3, floor: float = 1e-2):

@@ -351,3 +351,36 @@ void bqo_rmsnorm(const float* x, const float* g, int64_t M, int64_t K, float eps
     for (int64_t m = 0; m < M; ++m) r[m] = bqo_rms_inv(bqo_rms_sumsq(x + m * K, K), K, eps);
     bqo_rmsnorm_apply(x, g, r, M, K, y);
 }
+
+/* ------------------------------------------------- per-group W4A8 (g128) */
+
+/* The QQQ issue #15 tables compare per-channel W4A8 ("qqq") with a per-group
+ * variant ("qqq-g128"); the pages name the group size (128) but print no
+ * formula.  The plain reading used here: int4 weights with one scale per
+ * output channel n and group g of 128 consecutive k, int8 per-token
+ * activations, an exact integer sum per group, and the group scales applied
+ * to those sums:
+ *   acc_g[m,n] = sum_{k in group g} Aq[m,k] * W4[n,k]            (exact)
+ *   Y[m,n]     = sA[m] * sum_g sW[n,g] * acc_g[m,n]              (real)
+ * computed here in fp64 for the given rows (sW: [N][G] row-major). */
+void bqo_w4a8_group_linear(const int8_t* aq, const float* sa, const int8_t* w4, const float* sw,
+                           int64_t M, int64_t N, int64_t K, int64_t group, const int64_t* rows,
+                           int64_t nrows, double* y) {
+    const int64_t G = (K + group - 1) / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t m = rows[r];
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                int64_t acc = 0;
+                const int64_t k1 = (g + 1) * group < K ? (g + 1) * group : K;
+                for (int64_t k = g * group; k < k1; ++k)
+                    acc += (int64_t)aq[m * K + k] * (int64_t)w4[n * K + k];
+                sum += (double)sw[n * G + g] * (double)acc;
+            }
+            y[r * N + n] = (double)sa[m] * sum;
+        }
+    }
+    (void)M;
+}
