@@ -19,6 +19,7 @@ Operations (see the header for the exact contracts):
   fp8_linear_static       the same with a given (static) activation scale
   w8a16_linear            Y = sW[n] (A Wq^T), fp16 activations
   w4a8_linear             int4 x int8 with int32 accumulation
+  w4a8_group_linear       the same with a scale per channel and 128-k group
 """
 from __future__ import annotations
 
@@ -35,7 +36,7 @@ LIB_PATH = os.path.join(_HERE, "libbql.so")
 # bql_dtype
 F16, BF16, F32, E4M3, I8, I32, INT4 = 1, 2, 3, 4, 5, 6, 7
 # bql_wfmt
-WFMT = {"fp8_tensor": 1, "fp8_channel": 2, "int4_channel": 3}
+WFMT = {"fp8_tensor": 1, "fp8_channel": 2, "int4_channel": 3, "int4_group": 4}
 STATUS = {0: "BQL_OK", 1: "BQL_ERR_NULL", 2: "BQL_ERR_DTYPE", 3: "BQL_ERR_SHAPE",
           4: "BQL_ERR_ALIGN", 5: "BQL_ERR_WORKSPACE", 6: "BQL_ERR_HIP", 7: "BQL_ERR_ARG"}
 
@@ -79,6 +80,7 @@ SIGNATURES = {
     "bql_w8a16_linear": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "bql_w4a8_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "bql_w4a8_linear": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "bql_w4a8_group_linear": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -213,7 +215,7 @@ def rmsnorm_fp8_quantize_dynamic(x: torch.Tensor, g: torch.Tensor, eps: float,
 @dataclass
 class PackedWeight:
     packed: torch.Tensor   # uint8, private tile layout
-    scales: torch.Tensor   # fp32, [1] or [N], logical channel order
+    scales: torch.Tensor   # fp32, [1] or [N] in logical channel order; int4_group [K/128 * N]
     N: int
     K: int
     fmt: str
@@ -232,11 +234,12 @@ def prepack_weight(w: torch.Tensor, fmt: str = "fp8_tensor", scales: Optional[to
     """Quantize (when w is fp16/bf16) and pack an [N,K] weight.
 
     w: fp16/bf16 [N,K]; or E4M3 codes (uint8 / float8_e4m3fn) [N,K] with
-    `scales`; or, for fmt="int4_channel", logical int4 bytes uint8 [N,K/2]
+    `scales`; or, for fmt="int4_channel" / "int4_group", logical int4 bytes uint8 [N,K/2]
+    (int4_group: `scales` [N, K/128], stored group-major [K/128, N] in the result)
     with `scales` (pass K when w is flattened)."""
     _need_cuda(w, scales)
     L = lib()
-    if fmt == "int4_channel":
+    if fmt in ("int4_channel", "int4_group"):
         N = w.shape[0]
         K = K if K is not None else 2 * w.shape[1]
         wdt = INT4
@@ -244,7 +247,8 @@ def prepack_weight(w: torch.Tensor, fmt: str = "fp8_tensor", scales: Optional[to
         N, K = w.shape
         wdt = _TORCH_TO_BQL[w.dtype]
     packed = torch.empty(L.bql_packed_weight_bytes(N, K, WFMT[fmt]), dtype=torch.uint8, device=w.device)
-    sc = torch.empty(1 if fmt == "fp8_tensor" else N, dtype=torch.float32, device=w.device)
+    nsc = 1 if fmt == "fp8_tensor" else (N * (K // 128) if fmt == "int4_group" else N)
+    sc = torch.empty(nsc, dtype=torch.float32, device=w.device)
     ws, nb = _workspace(L.bql_prepack_workspace_size(N, K, WFMT[fmt]), w.device, None)
     sdt = 0 if scales is None else _TORCH_TO_BQL[scales.dtype]
     _check("bql_prepack_weight",
@@ -255,7 +259,7 @@ def prepack_weight(w: torch.Tensor, fmt: str = "fp8_tensor", scales: Optional[to
 
 def unpack_weight(pw: PackedWeight) -> torch.Tensor:
     """Logical codes: uint8 [N,K] (fp8) or logical int4 bytes uint8 [N,K/2]."""
-    shape = (pw.N, pw.K // 2) if pw.fmt == "int4_channel" else (pw.N, pw.K)
+    shape = (pw.N, pw.K // 2) if pw.fmt in ("int4_channel", "int4_group") else (pw.N, pw.K)
     out = torch.empty(shape, dtype=torch.uint8, device=pw.packed.device)
     _check("bql_unpack_weight",
            lib().bql_unpack_weight(_ptr(pw.packed), pw.N, pw.K, WFMT[pw.fmt], _ptr(out),
@@ -333,6 +337,27 @@ def w8a16_linear(a: torch.Tensor, pw: PackedWeight, out_dtype: torch.dtype = tor
     _check("bql_w8a16_linear",
            L.bql_w8a16_linear(_ptr(a), _ptr(pw.packed), _ptr(pw.scales), M, N, K, _ptr(out),
                               _TORCH_TO_BQL[out_dtype], _ptr(ws), nb, _stream(a.device)))
+    return out
+
+
+def w4a8_group_linear(aq: torch.Tensor, a_scales: torch.Tensor, pw: PackedWeight,
+                      out_dtype: torch.dtype = torch.float16, out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 [M,K] activations (per-row scales) x int4 weight with a scale per
+    output channel and 128-k group (prepacked as "int4_group")."""
+    _need_cuda(aq, a_scales, out, ws)
+    L = lib()
+    M, K = aq.shape
+    N = pw.N
+    if pw.fmt != "int4_group":
+        raise ValueError("w4a8_group_linear takes an int4_group weight")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=aq.device)
+    ws, nb = _workspace(L.bql_w4a8_linear_workspace_size(M, N, K), aq.device, ws)
+    _check("bql_w4a8_group_linear",
+           L.bql_w4a8_group_linear(_ptr(aq), _ptr(a_scales), _ptr(pw.packed), _ptr(pw.scales), M, N,
+                                   K, 128, _ptr(out), _TORCH_TO_BQL[out_dtype], _ptr(ws), nb,
+                                   _stream(aq.device)))
     return out
 
 

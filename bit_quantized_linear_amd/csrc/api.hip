@@ -192,7 +192,7 @@ bql_status bql_rmsnorm_fp8_quantize_dynamic(const void* x, const void* g, bql_dt
 size_t bql_packed_weight_bytes(int64_t N, int64_t K, bql_wfmt fmt) {
     if (N <= 0 || K <= 0) return 0;
     const size_t tiles = (size_t)((N + 15) / 16) * (size_t)ktiles(K);
-    return tiles * (fmt == BQL_WFMT_INT4_CHANNEL ? 1024 : 2048);
+    return tiles * ((fmt == BQL_WFMT_INT4_CHANNEL || fmt == BQL_WFMT_INT4_GROUP) ? 1024 : 2048);
 }
 
 size_t bql_prepack_workspace_size(int64_t N, int64_t K, bql_wfmt fmt) {
@@ -204,12 +204,25 @@ bql_status bql_prepack_weight(const void* w, bql_dtype wdt, int64_t N, int64_t K
                               const void* scales_in, bql_dtype sdt, void* packed,
                               float* scales_out, void* ws, size_t ws_bytes, bql_stream stream) {
     hipStream_t s = (hipStream_t)stream;
-    CHECK(fmt == BQL_WFMT_INT4_CHANNEL ? need_nk(N, K) : need_nk_fp8(N, K));
+    CHECK((fmt == BQL_WFMT_INT4_CHANNEL || fmt == BQL_WFMT_INT4_GROUP) ? need_nk(N, K)
+                                                                       : need_nk_fp8(N, K));
     CHECK(need_ptr(w, "w"));
     CHECK(need_ptr(packed, "packed"));
     CHECK(need_ptr(scales_out, "scales_out"));
-    if (fmt != BQL_WFMT_FP8_TENSOR && fmt != BQL_WFMT_FP8_CHANNEL && fmt != BQL_WFMT_INT4_CHANNEL)
+    if (fmt != BQL_WFMT_FP8_TENSOR && fmt != BQL_WFMT_FP8_CHANNEL && fmt != BQL_WFMT_INT4_CHANNEL &&
+        fmt != BQL_WFMT_INT4_GROUP)
         return fail(BQL_ERR_ARG, "unknown weight format %d", (int)fmt);
+    if (fmt == BQL_WFMT_INT4_GROUP) {
+        if (K % 128) return fail(BQL_ERR_SHAPE, "INT4_GROUP needs K=%lld a multiple of 128", (long long)K);
+        if (wdt != BQL_INT4) return fail(BQL_ERR_DTYPE, "INT4_GROUP takes a BQL_INT4 weight");
+        if (!scales_in) return fail(BQL_ERR_NULL, "INT4_GROUP needs scales_in");
+        if (sdt != BQL_F16 && sdt != BQL_F32) return fail(BQL_ERR_DTYPE, "scales must be BQL_F16 or BQL_F32");
+        CHECK(need_scalar(scales_in, "scales_in"));
+        if (sdt == BQL_F16 && (((uintptr_t)scales_in) & 1u)) return fail(BQL_ERR_ALIGN, "scales_in misaligned");
+        hipError_t e = bql::launch_group_scales(scales_in, sdt == BQL_F16 ? 1 : 3, N, K / 128, scales_out, s);
+        if (e == hipSuccess) e = bql::launch_prepack_int4((const uint8_t*)w, N, K, (uint8_t*)packed, s);
+        return hip_status(e);
+    }
     const int64_t nscales = fmt == BQL_WFMT_FP8_TENSOR ? 1 : N;
     if (scales_in) {
         if (sdt != BQL_F16 && sdt != BQL_F32) return fail(BQL_ERR_DTYPE, "scales must be BQL_F16 or BQL_F32");
@@ -245,10 +258,11 @@ bql_status bql_prepack_weight(const void* w, bql_dtype wdt, int64_t N, int64_t K
 
 bql_status bql_unpack_weight(const void* packed, int64_t N, int64_t K, bql_wfmt fmt, void* out,
                              bql_stream stream) {
-    CHECK(fmt == BQL_WFMT_INT4_CHANNEL ? need_nk(N, K) : need_nk_fp8(N, K));
+    const bool int4 = fmt == BQL_WFMT_INT4_CHANNEL || fmt == BQL_WFMT_INT4_GROUP;
+    CHECK(int4 ? need_nk(N, K) : need_nk_fp8(N, K));
     CHECK(need_ptr(packed, "packed"));
     CHECK(need_ptr(out, "out"));
-    if (fmt == BQL_WFMT_INT4_CHANNEL)
+    if (int4)
         return hip_status(bql::launch_unpack_int4((const uint8_t*)packed, N, K, (uint8_t*)out, (hipStream_t)stream));
     if (fmt == BQL_WFMT_FP8_TENSOR || fmt == BQL_WFMT_FP8_CHANNEL)
         return hip_status(bql::launch_unpack_fp8((const uint8_t*)packed, N, K, (uint8_t*)out, (hipStream_t)stream));
@@ -510,6 +524,53 @@ bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* 
     la.out_scale = nullptr;
     char* part = (char*)ws + align256(bql::packed_act_bytes(M, K));
     return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_W4A8),
+                                         (hipStream_t)stream));
+}
+
+bql_status bql_w4a8_group_linear(const int8_t* aq, const float* a_scales, const void* w_packed,
+                                 const float* w_scales, int64_t M, int64_t N, int64_t K,
+                                 int64_t group_size, void* y, bql_dtype ydt, void* ws,
+                                 size_t ws_bytes, bql_stream stream) {
+    CHECK(need_m(M));
+    CHECK(need_nk(N, K));
+    if (group_size != 128) return fail(BQL_ERR_ARG, "group_size must be 128");
+    if (K % 128 || K / 128 > bql::W4A8G_MAX_KT)
+        return fail(BQL_ERR_SHAPE, "K=%lld must be a multiple of 128, at most %d", (long long)K,
+                    128 * bql::W4A8G_MAX_KT);
+    if (N * (K / 128) * 4 >= (int64_t(1) << 31))
+        return fail(BQL_ERR_SHAPE, "N * K/128 group scales must fit in 2 GiB");
+    if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32)
+        return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16 or BQL_F32");
+    if (M == 0) return ok();
+    CHECK(need_ptr(aq, "aq"));
+    CHECK(need_ptr(w_packed, "w_packed"));
+    CHECK(need_ptr(y, "y"));
+    CHECK(need_ptr(a_scales, "a_scales"));
+    CHECK(need_ptr(w_scales, "w_scales"));
+    CHECK(need_ws(ws, ws_bytes, bql_w4a8_linear_workspace_size(M, N, K)));
+    uint8_t* aq_ws = (uint8_t*)ws;
+    // the small-M path reads the row-major int8 A where it is
+    const bool direct = bql::use_small_m(bql::V_W4A8G, M, N, K);
+    if (!direct) {
+        hipError_t e = bql::launch_pack_codes((const uint8_t*)aq, M, K, aq_ws, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    bql::LinearArgs la;
+    la.variant = bql::V_W4A8G;
+    la.a = direct ? (const void*)aq : (const void*)aq_ws;
+    la.a_rowmajor = direct ? 1 : 0;
+    la.w = (const uint8_t*)w_packed;
+    la.M = M;
+    la.N = N;
+    la.K = K;
+    la.y = y;
+    la.ydt = ydt;
+    la.a_scale = a_scales;
+    la.w_scale = w_scales;
+    la.w_per_channel = 1;
+    la.out_scale = nullptr;
+    char* part = (char*)ws + align256(bql::packed_act_bytes(M, K));
+    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_W4A8G),
                                          (hipStream_t)stream));
 }
 

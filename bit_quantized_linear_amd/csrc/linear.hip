@@ -80,6 +80,15 @@ template <> struct VT<V_W4A8> {
     using Acc = v4i;
     using E = int;
 };
+// Per-group W4A8: the B operand of the small-M kernels carries the k-tile's
+// group scale of the lane's channel as a second chunk (x component).
+template <> struct VT<V_W4A8G> {
+    static constexpr int B_TILE = INT4_TILE_BYTES;
+    static constexpr int A_CHUNKS = 2;
+    static constexpr int B_CHUNKS = 2;
+    using Acc = v4f;
+    using E = float;
+};
 
 // A operand of the small-M kernels, read through a buffer descriptor over
 // one 16-row tile of A (rows past M lie outside it and read as zero; k past
@@ -165,6 +174,20 @@ __device__ __forceinline__ void mma_w4a8(v4i& acc, const u4& alo, const u4& ahi,
     acc = mfma_i8(as_v4i(ahi), bhi, acc);
 }
 
+// One k-tile of per-group W4A8: the exact int32 sum of the tile (a 128-k
+// group, of 16 * W4 products) times s16 = group scale / 16, added in fp32.
+// |t| < 2^24 converts exactly, and s16 is exact wherever the scale is a
+// normal float above 2^-122, so each term is the single rounding of
+// (t / 16) * scale.  Two VALU instructions per accumulator per group, which
+// at the chip's rates already cost as much as the group's MFMAs.
+__device__ __forceinline__ void group_fold(v4f& acc, const u4& alo, const u4& ahi, const u4& b,
+                                           float s16) {
+    v4i t = v4i{0, 0, 0, 0};
+    mma_w4a8(t, alo, ahi, b);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf((float)t[r], s16, acc[r]);
+}
+
 template <int V>
 __device__ __forceinline__ void mma(typename VT<V>::Acc& acc, const u4 (&a)[VT<V>::A_CHUNKS],
                                     const u4 (&b)[VT<V>::B_CHUNKS]) {
@@ -172,6 +195,8 @@ __device__ __forceinline__ void mma(typename VT<V>::Acc& acc, const u4 (&a)[VT<V
         acc = mfma_fp8(as_v8i(a[0], a[1]), as_v8i(b[0], b[1]), acc);
     } else if constexpr (V == V_W4A8) {
         mma_w4a8(acc, a[0], a[1], b[0]);
+    } else if constexpr (V == V_W4A8G) {
+        group_fold(acc, a[0], a[1], b[0], __uint_as_float(b[1][0]) * 0.0625f);
     } else if constexpr (V == V_FP8X) {
         // four f16 MFMAs over k0+8q .. k0+8q+7 on losslessly decoded codes
         v8h ah[4], bh[4];
@@ -191,6 +216,7 @@ template <int V>
 __device__ __forceinline__ void finish(const LinParams& p, float sa, int64_t m, int64_t n,
                                        typename VT<V>::E v) {
     if constexpr (V == V_W4A8) epilogue_int(p.ep, m, n, v);
+    else if constexpr (V == V_W4A8G) store_out(p.ep, m, n, v * p.ep.a_scale[m]);
     else epilogue_float(p.ep, sa, m, n, v);
 }
 
@@ -204,6 +230,8 @@ __device__ __forceinline__ uint32_t out_bits(const Epilogue& ep, float sa, int64
         const int acc = v >> 4;
         if (ep.ydt == OUT_I32) return (uint32_t)acc;
         y = ((float)acc * ep.a_scale[m]) * ep.w_scale[n];
+    } else if constexpr (V == V_W4A8G) {
+        y = v * ep.a_scale[m];
     } else {
         y = (sa * ep.w_scale[ep.w_per_channel ? n : 0]) * v;
     }
@@ -228,7 +256,7 @@ __device__ __forceinline__ int out_size(int ydt) {
 // register room for two weight batches, A and the decoded operands without
 // spilling, and as many resident blocks as that leaves.
 constexpr int gemv_min_waves(int v, bool fused) {
-    return (fused || v == V_FP8 || v == V_W4A8) ? 6 : 5;
+    return (fused || v == V_FP8 || v == V_W4A8) ? 6 : 5;  // V_W4A8G: 5
 }
 
 template <int V, int NT, int WAVES, int U, bool FUSED>
@@ -253,6 +281,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
     const int64_t strips = ntiles - nt0 < NT ? ntiles - nt0 : NT;
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.w + nt0 * p.KT * BT), (short)0, (int)(strips * p.KT * BT), 0x00020000);
+    // V_W4A8G: group scales [KT][N] fp32
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.ep.w_scale, (short)0, (int)(V == V_W4A8G ? p.KT * p.N * 4 : 0), 0x00020000);
     // Weight tiles for k-tiles kt, kt + WAVES, ... (U of them) of this wave;
     // tiles past this split's k range (or past N) read as zero.
     auto load_batch = [&](int64_t kt, u4 (&b)[U][NT][VT<V>::B_CHUNKS]) {
@@ -263,10 +294,20 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
             for (int j = 0; j < NT; ++j) {
                 const bool ok = k < kt_end && j < strips;
                 const uint32_t off = (uint32_t)((j * p.KT + k) * BT) + lane * 16;
+                if constexpr (V == V_W4A8G) {
+                    // the weight tile, then this k-tile's scale of the lane's channel
+                    b[u][j][0] = __builtin_bit_cast(
+                        u4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ok ? off : OOB), 0, 2));
+                    const uint32_t soff = (uint32_t)((k * p.N + (nt0 + j) * TILE_N + (lane & 15)) * 4);
+                    b[u][j][1] = u4{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                                        rsc, (int)(ok ? soff : OOB), 0, 0),
+                                    0u, 0u, 0u};
+                } else {
 #pragma unroll
-                for (int c = 0; c < VT<V>::B_CHUNKS; ++c)
-                    b[u][j][c] = __builtin_bit_cast(
-                        u4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ok ? off + c * 1024 : OOB), 0, 2));
+                    for (int c = 0; c < VT<V>::B_CHUNKS; ++c)
+                        b[u][j][c] = __builtin_bit_cast(
+                            u4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ok ? off + c * 1024 : OOB), 0, 2));
+                }
             }
         }
     };
@@ -760,7 +801,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(LinParams p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-    auto compute = [&](const Frag& f) {
+    // V_W4A8G: the block's group scales / 16, [KT][BN] fp32 after the stage ring
+    [[maybe_unused]] const float* gsc = (const float*)(lds + C::LDS);
+    auto compute = [&](const Frag& f, [[maybe_unused]] int kt) {
         if constexpr (V == V_FP8) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -781,6 +824,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(LinParams p) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[i][j] = mfma_f16(ah[q], bh[j][q], acc[i][j]);
             }
+        } else if constexpr (V == V_W4A8G) {
+            float sc[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sc[j] = gsc[kt * BN + (wn * FN + j) * 16 + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) group_fold(acc[i][j], f.a[i][0], f.a[i][1], f.b[j][0], sc[j]);
         } else {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -792,6 +843,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(LinParams p) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
         if (s < KT) issue(s, s);
+    if constexpr (V == V_W4A8G) {
+        // stage the block's group scales (columns past N read as zero); the
+        // barrier's wait also retires the first stages' DMA, which the loop
+        // below would wait for next anyway
+        float* g = (float*)(lds + C::LDS);
+        for (int q = tid; q < KT * BN; q += 64 * NW) {
+            const int64_t n = n0 + q % BN;
+            g[q] = n < p.N ? p.ep.w_scale[(int64_t)(q / BN) * p.N + n] * 0.0625f : 0.0f;  // scale / 16
+        }
+        __syncthreads();
+    }
     // One k-step with a successor (kt + 1 < KT): fragments of kt are in
     // `cur`, those of kt+1 are read into `nxt` while the MFMAs of kt run.
     // The body has no branch around the LDS reads, so the MFMAs only wait
@@ -802,7 +864,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(LinParams p) {
         lds_barrier();
         if (kt + S < KT) issue(kt + S, kt % S);
         read_frags(kt + 1, nxt);
-        compute(cur);
+        compute(cur, kt);
     };
     Frag f0, f1;
     wait_behind(KT - 1 < S - 1 ? KT - 1 : S - 1);
@@ -816,9 +878,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(LinParams p) {
     }
     if (kt + 1 < KT) {
         step(kt, f0, f1);
-        compute(f1);
+        compute(f1, kt + 1);
     } else {
-        compute(f0);
+        compute(f0, kt);
     }
 
     // ---- epilogue (as gemm_kernel)
@@ -1159,6 +1221,9 @@ static hipError_t launch_gemm(const LinParams& p, hipStream_t stream) {
 template <int V, int BM, int BN, int WM, int WN, int S>
 static hipError_t launch_gemm_pipe(const LinParams& p, hipStream_t stream) {
     using C = GemmCfg<V, BM, BN, WM, WN, S>;
+    // V_W4A8G stages its group scales ([KT][BN] fp32) after the stage ring
+    constexpr int MAX_LDS = V == V_W4A8G ? C::LDS + BN * W4A8G_MAX_KT * 4 : C::LDS;
+    const int lds = V == V_W4A8G ? C::LDS + BN * (int)p.KT * 4 : C::LDS;
     static std::atomic<uint64_t> configured{0};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1166,12 +1231,12 @@ static hipError_t launch_gemm_pipe(const LinParams& p, hipStream_t stream) {
     const uint64_t bit = uint64_t(1) << (dev & 63);
     if (!(configured.load(std::memory_order_acquire) & bit)) {
         e = hipFuncSetAttribute((const void*)gemm_pipe_kernel<V, BM, BN, WM, WN, S>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, MAX_LDS);
         if (e != hipSuccess) return e;
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
     const int64_t blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    gemm_pipe_kernel<V, BM, BN, WM, WN, S><<<(unsigned)blocks, 64 * WM * WN, C::LDS, stream>>>(p);
+    gemm_pipe_kernel<V, BM, BN, WM, WN, S><<<(unsigned)blocks, 64 * WM * WN, lds, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -1213,7 +1278,7 @@ static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
         if (t128 <= CUS) return launch_gemm_pipe<V, 128, 128, 4, 2, 3>(p, stream);
         if (t256 >= 3 * CUS / 2) return launch_gemm<V, 256, 256, 4, 4, 2>(p, stream);
         return launch_gemm<V, 128, 128, 2, 4, 2>(p, stream);
-    } else {  // W4A8: best at every K = N in 4096..8192 measured
+    } else {  // W4A8 (and its per-group form): best at every K = N in 4096..8192 measured
         return launch_gemm_pipe<V, 128, 128, 2, 4, 2>(p, stream);
     }
 }
@@ -1254,6 +1319,7 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
             case V_FP8: return run_gemv<V_FP8, false>(p, stream);
             case V_FP8X: return run_gemv<V_FP8X, false>(p, stream);
             case V_W8A16: return run_gemv<V_W8A16, false>(p, stream);
+            case V_W4A8G: return run_gemv<V_W4A8G, false>(p, stream);
             default: return run_gemv<V_W4A8, false>(p, stream);
         }
     }
@@ -1263,6 +1329,7 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
     p.splits = 1;
     if (args.variant == V_FP8) return run_gemm<V_FP8>(p, stream);
     if (args.variant == V_FP8X) return run_gemm<V_FP8X>(p, stream);
+    if (args.variant == V_W4A8G) return run_gemm<V_W4A8G>(p, stream);
     return run_gemm<V_W4A8>(p, stream);
 }
 

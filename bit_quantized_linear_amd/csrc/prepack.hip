@@ -12,6 +12,7 @@
 // on optimum-quanto PR #241).
 #include "device.h"
 #include "kernels.h"
+#include "skinny.h"
 
 namespace bql {
 
@@ -42,6 +43,17 @@ __global__ void convert_scales_kernel(const void* __restrict__ s, int sdt, int64
     int64_t i = (int64_t)blockIdx.x * PT + threadIdx.x;
     if (i >= count) return;
     out[i] = sdt == 1 ? to_f32<IN_F16>(((const uint16_t*)s)[i]) : ((const float*)s)[i];
+}
+
+// Per-group scales, given [N][G] (fp16 or fp32), stored [G][N] in fp32 so
+// that the kernels read one k-tile's scales of consecutive channels together.
+__global__ void group_scales_kernel(const void* __restrict__ s, int sdt, int64_t N, int64_t G,
+                                    float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * PT + threadIdx.x;  // output index g * N + n
+    if (i >= N * G) return;
+    const int64_t g = i / N, n = i % N;
+    const int64_t src = n * G + g;
+    out[i] = sdt == 1 ? to_f32<IN_F16>(((const uint16_t*)s)[src]) : ((const float*)s)[src];
 }
 
 // One thread per 16-byte chunk of the packed layout.
@@ -164,6 +176,12 @@ hipError_t launch_row_scales(const void* w, int wdt, int64_t N, int64_t K, float
 hipError_t launch_convert_scales(const void* s, int sdt, int64_t count, float* out,
                                  hipStream_t stream) {
     convert_scales_kernel<<<blocks_for(count), PT, 0, stream>>>(s, sdt, count, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_scales(const void* s, int sdt, int64_t N, int64_t G, float* out,
+                               hipStream_t stream) {
+    group_scales_kernel<<<blocks_for(N * G), PT, 0, stream>>>(s, sdt, N, G, out);
     return hipGetLastError();
 }
 

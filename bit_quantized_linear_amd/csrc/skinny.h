@@ -11,6 +11,11 @@ namespace bql {
 // Widest N the small-N path serves (one 16-channel strip, N < 16).
 constexpr int64_t SKINNY_MAX_N = 15;
 
+// Per-group W4A8 scales [N][G] (sdt 1 = fp16, 3 = fp32) -> [G][N] fp32
+// (prepack.hip).
+hipError_t launch_group_scales(const void* s, int sdt, int64_t N, int64_t G, float* out,
+                               hipStream_t stream);
+
 // Per-block amax partials of numel 16-bit values (quant.hip); returns the
 // number of partials written (at most 1024).
 int launch_amax_partials(const void* x, int64_t numel, uint32_t* partial, hipStream_t stream);

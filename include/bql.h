@@ -86,7 +86,9 @@ typedef enum bql_dtype {
 typedef enum bql_wfmt {
     BQL_WFMT_FP8_TENSOR = 1,  /* E4M3 weight, one fp32 scale */
     BQL_WFMT_FP8_CHANNEL = 2, /* E4M3 weight, fp32 scale per output channel n */
-    BQL_WFMT_INT4_CHANNEL = 3 /* int4 weight, fp32 scale per output channel n */
+    BQL_WFMT_INT4_CHANNEL = 3, /* int4 weight, fp32 scale per output channel n */
+    BQL_WFMT_INT4_GROUP = 4    /* int4 weight, fp32 scale per output channel n and
+                                  group of 128 consecutive k */
 } bql_wfmt;
 
 /* How the fp8 linear sums its products (torch._scaled_mm, which the vLLM
@@ -210,12 +212,14 @@ size_t bql_prepack_workspace_size(int64_t N, int64_t K, bql_wfmt fmt);
  *      BQL_INT4 (logical packing, N*K/2 bytes) with fmt INT4_CHANNEL
  *      (scales_in needed).
  *   scales_in: NULL, or 1 (FP8_TENSOR) / N (*_CHANNEL) scales of dtype sdt
- *      (BQL_F16 or BQL_F32).  NULL with a float weight means
+ *      (BQL_F16 or BQL_F32); INT4_GROUP takes N * K/128 scales, [N][K/128]
+ *      row-major (required; K a multiple of 128).  NULL with a float weight means
  *      scale = fp32(amax / 448) over the whole tensor (FP8_TENSOR) or over
  *      each row n (FP8_CHANNEL), 1.0 where the amax is 0.  The float weight
  *      is then quantized as Wq = E4M3(fp32(W / scale)).
  *   packed: bql_packed_weight_bytes(N, K, fmt) bytes, private layout.
- *   scales_out: fp32, 1 (FP8_TENSOR) or N entries, in logical n order.
+ *   scales_out: fp32, 1 (FP8_TENSOR) or N entries, in logical n order;
+ *      INT4_GROUP: N * K/128 entries stored [K/128][N] (group-major).
  *   ws: >= bql_prepack_workspace_size(N, K, fmt) bytes. */
 bql_status bql_prepack_weight(const void* w, bql_dtype wdt, int64_t N, int64_t K,
                               bql_wfmt fmt, const void* scales_in, bql_dtype sdt,
@@ -299,6 +303,22 @@ bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* 
                            const float* w_scales, int64_t M, int64_t N, int64_t K,
                            void* y, bql_dtype ydt, void* ws, size_t ws_bytes,
                            bql_stream stream);
+
+/* Per-group W4A8 linear (QQQ issue #15: the "qqq-g128" columns, read as one
+ * scale per output channel n and group g of 128 consecutive k):
+ *   acc_g[m,n] = sum_{k in g} Aq[m,k] * W4[n,k] in int32 (exact; the int4
+ *   values are used as 16*W4 in the int8 MMA and each group's sum is
+ *   divided by 16 exactly),
+ *   Y[m,n] = fp32(sum_g fp32(acc_g) * sW[n,g], summed in g order) * sA[m].
+ *   aq: [M,K] int8; a_scales: M fp32; w_packed: INT4_GROUP layout;
+ *   w_scales: the scales_out of that prepack ([K/128][N] fp32).
+ *   group_size must be 128; K a multiple of 128, at most 16384.
+ *   y: [M,N] of ydt = BQL_F16, BQL_BF16 or BQL_F32.
+ *   ws: >= bql_w4a8_linear_workspace_size(M, N, K) bytes. */
+bql_status bql_w4a8_group_linear(const int8_t* aq, const float* a_scales, const void* w_packed,
+                                 const float* w_scales, int64_t M, int64_t N, int64_t K,
+                                 int64_t group_size, void* y, bql_dtype ydt, void* ws,
+                                 size_t ws_bytes, bql_stream stream);
 
 #ifdef __cplusplus
 }

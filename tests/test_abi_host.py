@@ -120,6 +120,28 @@ def test_quantizer_validation(L):
     assert p(A16, 1, 0, 32, A16, A16, None) == OK
 
 
+def test_w4a8_group_validation(L):
+    f = L.bql_w4a8_group_linear
+    ws = L.bql_w4a8_linear_workspace_size(4, 64, 256)
+
+    def call(aq=A16, sa=A16, w=A16, sw=A16, M=4, N=64, K=256, g=128, y=A16, ydt=1, work=A16,
+             wsb=ws):
+        return f(aq, sa, w, sw, M, N, K, g, y, ydt, work, wsb, None)
+    assert call(g=64) == ERR_ARG
+    assert call(K=272) == ERR_SHAPE                # not a multiple of 128
+    assert call(K=128 * 129) == ERR_SHAPE          # above the staged-scale limit
+    assert call(ydt=6) == ERR_DTYPE                # no raw int32 output per group
+    assert call(sa=None) == ERR_NULL
+    assert call(sw=None) == ERR_NULL
+    assert call(work=None) == ERR_WS
+    assert call(M=0, work=None, wsb=0) == OK
+    assert L.bql_packed_weight_bytes(64, 256, 4) == L.bql_packed_weight_bytes(64, 256, 3)
+    p = L.bql_prepack_weight
+    assert p(A16, 7, 64, 272, 4, A16, 1, A16, A16, None, 0, None) == ERR_SHAPE
+    assert p(A16, 7, 64, 256, 4, None, 1, A16, A16, None, 0, None) == ERR_NULL
+    assert p(A16, 1, 64, 256, 4, A16, 1, A16, A16, None, 0, None) == ERR_DTYPE
+
+
 def test_small_n_shape_rule(L):
     # the fp8 formats take 1 <= N <= 15 (one padded strip); others keep N % 16
     assert L.bql_packed_weight_bytes(8, 4096, 1) == 32 * 2048
