@@ -138,37 +138,76 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
 // row l % 16 and k = 32*(l/16) + 16*h + j.  Columns k >= K up to the tile
 // edge and rows past M in the last strip hold zero codes.
 
-// the tile loop of cast_e4m3_packed_kernel, for a given x -> x/s
+// The 32 inputs of lane (r, g) for packed tile t: row 16 mt + r, k = 128 kt
+// + 32 g .. +31, as two halves of two 16-byte loads.  Rows past M and k
+// past K (K is a multiple of 16) read as zero; every load is issued (from a
+// valid address when out of range) so that none sits in a branch.
+struct TileIn {
+    u4 v[2][2];
+};
+
+__device__ __forceinline__ void load_tile_in(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                             int64_t KT, int64_t t, int r, int g, TileIn& in) {
+    const int64_t mt = t / KT, kt = t % KT;
+    const int64_t m = mt * 16 + r, k = kt * 128 + 32 * g;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bool ok = m < M && k + 16 * h < K;
+        const u4* src = (const u4*)(ok ? x + m * K + k + 16 * h : x);
+        const u4 v0 = __builtin_nontemporal_load(src), v1 = __builtin_nontemporal_load(src + 1);
+        in.v[h][0] = ok ? v0 : u4{0u, 0u, 0u, 0u};
+        in.v[h][1] = ok ? v1 : u4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Codes of one tile's inputs, stored at tile t + 16 l (k .. k+15) and
+// tile t + 1024 + 16 l (k+16 .. k+31).  Zero inputs give zero codes.
+template <int DT, class Div>
+__device__ __forceinline__ void store_tile_codes(const TileIn& in, uint8_t* __restrict__ xq,
+                                                 int64_t t, int lane, Div div) {
+    u4 out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t c[8];  // code pairs
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u4& v0 = in.v[h][0];
+            const u4& v1 = in.v[h][1];
+            c[j] = e4m3_encode2(div(to_f32<DT>(v0[j] & 0xFFFFu)), div(to_f32<DT>(v0[j] >> 16)));
+            c[4 + j] = e4m3_encode2(div(to_f32<DT>(v1[j] & 0xFFFFu)), div(to_f32<DT>(v1[j] >> 16)));
+        }
+        out[h] = u4{c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+    }
+    uint8_t* tile = xq + t * 2048 + lane * 16;
+    *(u4*)tile = out[0];
+    *(u4*)(tile + 1024) = out[1];
+}
+
+// The tile loop of the packed casts, for a given x -> x/s: wave w of block b
+// takes tiles t0 = b * WPB + w, t0 + gridDim.x * WPB, ...; the inputs of t0
+// were requested by the caller before it had the scale (`first`).
 template <int DT, class Div>
 __device__ __forceinline__ void cast_packed_tiles(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                   int64_t KT, uint8_t* __restrict__ xq, int64_t tiles,
-                                                  int lane, int r, int g, Div div) {
+                                                  int lane, int r, int g, const TileIn& first, Div div) {
     constexpr int WPB = QT / 64;
-    for (int64_t t = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6); t < tiles;
-         t += (int64_t)gridDim.x * WPB) {
-        const int64_t mt = t / KT, kt = t % KT;
-        const int64_t m = mt * 16 + r, k = kt * 128 + 32 * g;
-        u4 out[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t c[8];  // code pairs
-#pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = 0;
-            if (m < M && k + 16 * h < K) {
-                const u4* src = (const u4*)(x + m * K + k + 16 * h);
-                const u4 v0 = __builtin_nontemporal_load(src), v1 = __builtin_nontemporal_load(src + 1);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    c[j] = e4m3_encode2(div(to_f32<DT>(v0[j] & 0xFFFFu)), div(to_f32<DT>(v0[j] >> 16)));
-                    c[4 + j] = e4m3_encode2(div(to_f32<DT>(v1[j] & 0xFFFFu)), div(to_f32<DT>(v1[j] >> 16)));
-                }
-            }
-            out[h] = u4{c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
-        }
-        uint8_t* tile = xq + t * 2048 + lane * 16;
-        *(u4*)tile = out[0];
-        *(u4*)(tile + 1024) = out[1];
+    const int64_t stride = (int64_t)gridDim.x * WPB;
+    int64_t t = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
+    if (t >= tiles) return;
+    store_tile_codes<DT>(first, xq, t, lane, div);
+    for (t += stride; t < tiles; t += stride) {
+        TileIn in;
+        load_tile_in(x, M, K, KT, t, r, g, in);
+        store_tile_codes<DT>(in, xq, t, lane, div);
     }
+}
+
+// Blocks of the packed casts: one tile per wave up to 8192 blocks (more
+// waves in flight measured faster than fewer waves that each prefetch their
+// next tile).
+static int64_t packed_cast_blocks(int64_t tiles) {
+    const int64_t blocks = (tiles + QT / 64 - 1) / (QT / 64);
+    return blocks < 8192 ? blocks : 8192;
 }
 
 // One wave per 16 x 128 packed tile (row tile mt, k-tile kt), grid-stride
@@ -186,19 +225,25 @@ __global__ __launch_bounds__(QT) void cast_e4m3_packed_kernel(const uint16_t* __
                                                               float* __restrict__ scale_out,
                                                               float* __restrict__ scale_ws) {
     __shared__ uint32_t sh[16];
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int64_t tiles = ((M + 15) / 16) * KT;
+    // the first tile's inputs are requested before the partials are folded,
+    // so their HBM latency overlaps the fold's
+    const int64_t t0 = (int64_t)blockIdx.x * (QT / 64) + (threadIdx.x >> 6);
+    TileIn first;
+    load_tile_in(x, M, K, KT, t0 < tiles ? t0 : 0, r, g, first);
     const float s = scale_from_partials<DT>(partial, nparts, 448.0f, sh);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (scale_out) *scale_out = s;
         if (scale_ws) *scale_ws = s;
     }
-    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    const int64_t tiles = ((M + 15) / 16) * KT;
     const float y = 1.0f / s;
     if (recip_div_ok(s))
-        cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g,
+        cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, first,
                               [&](float v) { return div_by_scale(v, s, y); });
     else
-        cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, [&](float v) { return v / s; });
+        cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, first,
+                              [&](float v) { return v / s; });
 }
 
 // Static-scale cast into the packed layout: s is given (checkpoint
@@ -211,8 +256,11 @@ __global__ __launch_bounds__(QT) void cast_e4m3_packed_static_kernel(const uint1
                                                                      uint8_t* __restrict__ xq) {
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const int64_t tiles = ((M + 15) / 16) * KT;
+    const int64_t t0 = (int64_t)blockIdx.x * (QT / 64) + (threadIdx.x >> 6);
+    TileIn first;
+    load_tile_in(x, M, K, KT, t0 < tiles ? t0 : 0, r, g, first);
     const double inv = 1.0 / (double)*given;
-    cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g,
+    cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, first,
                           [&](float v) { return quot_f32(v, inv); });
 }
 
@@ -251,8 +299,7 @@ hipError_t launch_quant_dynamic_packed(const void* x, int xdt, int64_t M, int64_
     const int nb = amax_blocks(numel);
     amax_partial_kernel<<<nb, QT, 0, stream>>>((const uint16_t*)x, numel, partial);
     const int64_t KT = (K + 127) / 128;
-    int64_t blocks = (((M + 15) / 16) * KT + QT / 64 - 1) / (QT / 64);
-    if (blocks > 8192) blocks = 8192;
+    const int64_t blocks = packed_cast_blocks(((M + 15) / 16) * KT);
     if (xdt == IN_BF16)
         cast_e4m3_packed_kernel<IN_BF16><<<(unsigned)blocks, QT, 0, stream>>>(
             (const uint16_t*)x, M, K, KT, partial, nb, xq, scale_out, scale_ws);
@@ -318,8 +365,7 @@ hipError_t launch_quant_static(const void* x, int xdt, int64_t numel, const floa
 hipError_t launch_quant_static_packed(const void* x, int xdt, int64_t M, int64_t K,
                                       const float* scale, uint8_t* xq, hipStream_t stream) {
     const int64_t KT = (K + 127) / 128;
-    int64_t blocks = (((M + 15) / 16) * KT + QT / 64 - 1) / (QT / 64);
-    if (blocks > 8192) blocks = 8192;
+    const int64_t blocks = packed_cast_blocks(((M + 15) / 16) * KT);
     if (xdt == IN_BF16)
         cast_e4m3_packed_static_kernel<IN_BF16><<<(unsigned)blocks, QT, 0, stream>>>(
             (const uint16_t*)x, M, K, KT, scale, xq);
