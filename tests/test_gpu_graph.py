@@ -1,9 +1,10 @@
 """Captured HIP graphs of the linears replay to the eager result.
 
 Every path is captured once (small-M fused and split-K, the tiled kernel,
-exact and fast accumulation, W8A16, W4A8) and replayed several times with
-eager work and synchronizations in between; each replay must equal the
-eager output bit for bit (all kernels are deterministic).
+exact and fast accumulation, W8A16, W4A8, the static-scale linear, the
+small-N linear, the fused RMSNorm quantizers, per-group W4A8) and replayed
+several times with eager work and synchronizations in between; each replay
+must equal the eager output bit for bit (all kernels are deterministic).
 """
 import numpy as np
 import pytest
@@ -77,3 +78,68 @@ def test_w8a16_and_w4a8_graph():
                       device=DEV)
     _replays_match(lambda: bql.w4a8_linear(aq, None, pw4, out_dtype=torch.int32, out=out4, ws=ws4), out4,
                    lambda: bql.w4a8_linear(aq, None, pw4, out_dtype=torch.int32))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (16, 1024, 1024), (512, 1024, 4096)])
+def test_fp8_linear_static_graph(M, N, K):
+    g = wl.rng(13, M, N)
+    pw = bql.prepack_weight(dev16(wl.weight(g, N, K, "bf16"), "bf16"), "fp8_channel")
+    a = dev16(wl.activation(g, M, K, "bf16", "channels"), "bf16")
+    sa = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=DEV)
+    _replays_match(lambda: bql.fp8_linear_static(a, pw, sa, out_dtype=torch.bfloat16, out=out, ws=ws),
+                   out, lambda: bql.fp8_linear_static(a * 2, pw, sa, out_dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("M", [1, 300])
+def test_small_n_graph(M):
+    N, K = 8, 4096
+    g = wl.rng(14, M)
+    pw = bql.prepack_weight(dev16(wl.weight(g, N, K, "bf16"), "bf16"), "fp8_tensor")
+    a = dev16(wl.activation(g, M, K, "bf16", "channels"), "bf16")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=DEV)
+    _replays_match(lambda: bql.fp8_linear(a, pw, out_dtype=torch.bfloat16, out=out, ws=ws), out,
+                   lambda: bql.fp8_linear(a * 3, pw, out_dtype=torch.bfloat16))
+
+
+def test_rmsnorm_quantizers_graph():
+    M, K = 256, 4096
+    g = wl.rng(15, 0)
+    x = dev16(wl.activation(g, M, K, "bf16", "channels"), "bf16")
+    gw = dev16(wl.norm_weight(g, K, "bf16"), "bf16")
+    q8 = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    s8 = torch.empty(M, dtype=torch.float32, device=DEV)
+    L = bql.lib()
+
+    def run8():
+        bql._check("int8", L.bql_rmsnorm_int8_quantize_per_token(
+            bql._ptr(x), bql._ptr(gw), bql.BF16, M, K, 1e-5, bql._ptr(q8), bql._ptr(s8), None,
+            bql._stream(x.device)))
+    _replays_match(run8, q8, lambda: bql.rmsnorm_int8_quantize_per_token(x * 2, gw, 1e-5))
+    qf = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    sf = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(256, L.bql_rmsnorm_quantize_workspace_size(M)), dtype=torch.uint8, device=DEV)
+
+    def runf():
+        bql._check("fp8", L.bql_rmsnorm_fp8_quantize_dynamic(
+            bql._ptr(x), bql._ptr(gw), bql.BF16, M, K, 1e-5, bql._ptr(qf), bql._ptr(sf), None,
+            bql._ptr(ws), ws.numel(), bql._stream(x.device)))
+    _replays_match(runf, qf, lambda: bql.rmsnorm_fp8_quantize_dynamic(x * 3, gw, 1e-5))
+
+
+@pytest.mark.parametrize("M", [1, 200])
+def test_w4a8_group_graph(M):
+    N, K = 1024, 1024
+    g = wl.rng(16, M)
+    w4 = wl.int4_weight(g, N, K)
+    sc = dev((g.uniform(0.5, 2.0, size=(N, K // 128)) * 2.0 ** -8).astype(np.float32))
+    pw = bql.prepack_weight(dev(wl.pack_int4(w4).reshape(N, K // 2)), "int4_group", scales=sc)
+    aq = dev(g.integers(-127, 128, (M, K), dtype=np.int8))
+    sa = dev(g.uniform(1e-3, 1e-1, size=M).astype(np.float32))
+    out = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    ws = torch.empty(max(256, bql.lib().bql_w4a8_linear_workspace_size(M, N, K)), dtype=torch.uint8,
+                     device=DEV)
+    _replays_match(lambda: bql.w4a8_group_linear(aq, sa, pw, out=out, ws=ws), out,
+                   lambda: bql.w4a8_group_linear(aq, sa * 2, pw))
