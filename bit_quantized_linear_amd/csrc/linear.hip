@@ -1273,6 +1273,13 @@ static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
     if constexpr (V == V_FP8X) {
         if (t128 <= CUS) return launch_gemm_ks<128, 128, 2, 2, 2>(p, stream);
+        // Two blocks share a CU, so the busiest CU carries ceil(tiles / CUs)
+        // tiles: 128x96 tiles win where they even that out (M = 1024, N =
+        // 6144: 384 tiles of 128 columns leave half the CUs with two, 512
+        // tiles of 96 give every CU two of three quarters the width).
+        const int64_t t96 = ((p.M + 127) / 128) * ((p.N + 95) / 96);
+        if (((t96 + CUS - 1) / CUS) * 96 < ((t128 + CUS - 1) / CUS) * 128)
+            return launch_gemm<V, 128, 96, 2, 2, 2>(p, stream);
         return launch_gemm<V, 128, 128, 2, 2, 2>(p, stream);
     } else if constexpr (V == V_FP8) {
         if (t128 <= CUS) return launch_gemm_pipe<V, 128, 128, 4, 2, 3>(p, stream);
