@@ -49,6 +49,8 @@ SMALL_STEPS_PER_GRAPH = 4
 
 
 CALIBRATION_COPY_BYTES = 256 * 2 ** 20
+CUS_MI355X = 256
+XCDS_MI355X = 8
 # sources the tiled GEMM kernels are built from; a traffic summary is only
 # used while they are unchanged
 KERNEL_SOURCES = ["bit_quantized_linear_amd/csrc/linear.hip",
@@ -133,6 +135,61 @@ def summarize_traffic(fetch_dir, write_dir):
     with open(TRAFFIC_SUMMARY, "w") as fh:
         fh.write("\n".join(text) + "\n")
     print("\n".join(text))
+
+
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_m1024_n28672_k4096_mfma_counters.txt")
+MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def summarize_mfma(pmc_dir):
+    """Matrix-core counters of the two dominant GEMMs from one rocprofv3
+    --pmc run of `bench.py --roofline-only`: MFMA ops per launch (the MOPS
+    counters count 512 ops per unit) against the algorithmic 2*M*N*K, and the
+    matrix cores' busy cycles per CU against the GPU's active cycles."""
+    rows = []
+    for root, _, files in os.walk(pmc_dir):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    rows += list(csv.DictReader(fh))
+    per = {}
+    for r in rows:
+        k = (int(r["Dispatch_Id"]), r["Kernel_Name"].replace(" ", ""))
+        per.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+        per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+    flops = 2 * 1024 * 28672 * 4096
+    lines = ["# Matrix-core counters of the dominant GEMM launches, M=1024 N=28672 K=4096",
+             "# (tiled GEMM, pre-quantized A; exact = f16 MFMA on decoded fp8, fast = fp8 MFMA)",
+             "commands (repo root; cd /tmp && export TMPDIR=/tmp first, then back):",
+             "  rocprofv3 --pmc " + " ".join(MFMA_COUNTERS)
+             + " -f csv -d gpurun_out/pmc_mfma -o run -- python3 bench.py --roofline-only",
+             "  python3 bench.py --summarize-mfma gpurun_out/pmc_mfma",
+             f"source_sha256: {kernel_source_hash()}",
+             f"algorithmic flops per launch (2*M*N*K): {flops}"]
+    for tag, sig, mops in (("exact", "gemm_kernel<3,", "SQ_INSTS_VALU_MFMA_MOPS_F16"),
+                           ("fast", "gemm_kernel<0,", "SQ_INSTS_VALU_MFMA_MOPS_F8")):
+        ds = [v for (i, name), v in per.items() if sig in name]
+        if not ds:
+            raise SystemExit(f"no {sig} dispatches in {pmc_dir}")
+        n = len(ds)
+        avg = {c: sum(d.get(c, 0.0) for d in ds) / n for c in MFMA_COUNTERS}
+        ops = avg[mops] * 512
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs (each reads about clock x
+        # duration); MFMA busy cycles are summed over the 4 SIMDs of every CU
+        active = avg["GRBM_GUI_ACTIVE"] / XCDS_MI355X
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * CUS_MI355X * 4) if active else float("nan")
+        lines += [f"{tag}: {n} dispatches",
+                  f"  {mops} x 512 = {ops:.4g} ops per launch ({ops / flops:.4f} of 2*M*N*K)",
+                  f"  SQ_VALU_MFMA_BUSY_CYCLES = {avg['SQ_VALU_MFMA_BUSY_CYCLES']:.4g}, "
+                  f"SQ_BUSY_CU_CYCLES = {avg['SQ_BUSY_CU_CYCLES']:.4g}, "
+                  f"GRBM_GUI_ACTIVE = {avg['GRBM_GUI_ACTIVE']:.4g}",
+                  f"  matrix cores busy: MFMA_BUSY / (GUI_ACTIVE / {XCDS_MI355X} XCDs * {CUS_MI355X} CUs"
+                  f" * 4 SIMDs) = {busy:.4f}  (the counters slow the kernel; a fraction of its"
+                  f" own active cycles)"]
+    with open(MFMA_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def algorithmic_bytes_gemm(M, N, K):
@@ -525,11 +582,16 @@ def main():
                     help="only the per-group W4A8 leg (for a rocprofv3 run of it)")
     ap.add_argument("--small-n-only", action="store_true",
                     help="only the small-N (MoE router) leg (for a rocprofv3 run of it)")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="write the matrix-core counter summary from one rocprofv3 --pmc run")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc output folders")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
