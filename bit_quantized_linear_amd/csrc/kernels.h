@@ -42,7 +42,8 @@ hipError_t launch_tensor_scale(const void* x, int xdt, int64_t numel, float qmax
 
 // ----------------------------------------------------------- norm_quant.hip
 // RMSNorm fused with per-token int8 (one launch) or per-tensor E4M3 (two
-// launches; ws holds M row maxima and M inverse RMS values).  K <= 32768.
+// launches; ws holds one maximum per row-kernel block, at most M, and the M
+// inverse RMS values).  K <= 32768.
 constexpr int64_t RMSNORM_MAX_K = 32768;
 size_t rmsnorm_quant_ws_bytes(int64_t M);
 hipError_t launch_rmsnorm_int8(const void* x, const void* g, int xdt, int64_t M, int64_t K,
