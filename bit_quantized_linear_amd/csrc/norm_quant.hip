@@ -14,7 +14,7 @@
 //   per-tensor E4M3 (vLLM PR #4118):    s = amax / 448,       q = E4M3(y / s);
 // with IEEE fp32 divisions y / s, formed as quot_f32 (device.h) forms them.
 //
-// Kernels.  Grids are persistent (at most 512 blocks of 256 threads, or 256
+// Kernels.  Grids are persistent (at most 1024 blocks of 256 threads, or 512
 // of 1024 threads for K > 8192); a block walks rows gridDim.x apart with
 // each row in registers (up to four 16-byte chunks of 8 elements per
 // thread), g held for all its rows, and the next row requested before the
@@ -23,7 +23,7 @@
 // Per-token int8 is one launch.  Per-tensor E4M3 has a grid-wide dependency
 // (the amax of y over all rows), so it is two launches: the row kernel
 // stores r[m] and the maximum of |y| over each block's rows in the
-// workspace, and every block of the cast kernel folds those (at most 512)
+// workspace, and every block of the cast kernel folds those (at most 1024)
 // maxima itself before it re-reads its rows, recomputes y and writes the
 // codes.  No atomics, nothing to zero beforehand, and results do not depend
 // on the order in which blocks run.
@@ -248,8 +248,8 @@ size_t rmsnorm_quant_ws_bytes(int64_t M) {
 // up to K = 8192, then 1024 threads with 2 or 4 chunks up to K = 32768.
 // Grids are persistent: at most NQ_BLOCKS_256 (or NQ_BLOCKS_1024) blocks,
 // each walking rows gridDim.x apart.
-constexpr int64_t NQ_BLOCKS_256 = 512;
-constexpr int64_t NQ_BLOCKS_1024 = 256;
+constexpr int64_t NQ_BLOCKS_256 = 1024;
+constexpr int64_t NQ_BLOCKS_1024 = 512;
 
 static unsigned nq_grid(int64_t M, int BT) {
     const int64_t cap = BT == 256 ? NQ_BLOCKS_256 : NQ_BLOCKS_1024;
