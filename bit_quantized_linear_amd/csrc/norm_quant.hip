@@ -19,7 +19,8 @@
 // each row in registers (up to four 16-byte chunks of 8 elements per
 // thread), g held for all its rows, and the next row requested before the
 // current one is reduced and quantized.  The sum of squares and the row
-// maximum are wave shuffles plus a fixed-order fold over the block's waves.
+// maximum are DPP folds within each wave plus a fixed-order fold over the
+// block's waves, one barrier each.
 // Per-token int8 is one launch.  Per-tensor E4M3 has a grid-wide dependency
 // (the amax of y over all rows), so it is two launches: the row kernel
 // stores r[m] and the maximum of |y| over each block's rows in the
@@ -33,19 +34,82 @@
 namespace bql {
 
 
-// Sum over the block in a fixed order, returned to every thread.
-// `sh` holds >= 16 doubles.
-__device__ __forceinline__ double block_sum_f64(double v, double* sh) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nw = (blockDim.x + 63) >> 6;
-    __syncthreads();
-    if (lane == 0) sh[wave] = v;
+// Wave folds with DPP lane moves inside each 16-lane row: quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  At every
+// step a lane and its partner combine the same two values, so after the
+// four steps every lane of a row holds the row's fold (an IEEE sum is
+// commutative, so partners agree bit for bit).  The four rows are then
+// combined from lanes 0, 16, 32, 48 in a fixed order, giving a value that
+// is uniform over the wave.  No LDS round trips, unlike lane shuffles.
+constexpr int DPP_QP_1032 = 0xB1, DPP_QP_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,
+              DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64<DPP_QP_1032>(v);
+    v += dpp_f64<DPP_QP_2301>(v);
+    v += dpp_f64<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_ROW_MIRROR>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+    v = umax(v, dpp_u32<DPP_QP_1032>(v));
+    v = umax(v, dpp_u32<DPP_QP_2301>(v));
+    v = umax(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+    v = umax(v, dpp_u32<DPP_ROW_MIRROR>(v));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return umax(umax(r0, r1), umax(r2, r3));
+}
+
+// Block folds with one barrier: each wave's value goes to sh[wave], then
+// every thread folds sh[0 .. BT/64) in order.  A call's writes could race
+// with the reads of the call just before it on the same buffer, so
+// consecutive calls in a block must use different buffers (any two calls
+// further apart are separated by the barrier of the call between them).
+template <int BT>
+__device__ __forceinline__ double block_sum_1b(double v, double* sh) {
+    v = wave_sum_f64(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
     double s = 0.0;
-    for (int i = 0; i < nw; ++i) s += sh[i];
+#pragma unroll
+    for (int i = 0; i < BT / 64; ++i) s += sh[i];
     return s;
+}
+
+template <int BT>
+__device__ __forceinline__ uint32_t block_max_1b(uint32_t v, uint32_t* sh) {
+    v = wave_max_dpp(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < BT / 64; ++i) m = umax(m, sh[i]);
+    return m;
 }
 
 template <int DT>
@@ -93,12 +157,15 @@ __global__ __launch_bounds__(BT) void rmsnorm_rows_kernel(const uint16_t* __rest
                                                           float* __restrict__ inv_rms,
                                                           uint32_t* __restrict__ partial,
                                                           float* __restrict__ r_ws) {
-    __shared__ double shd[16];
-    __shared__ uint32_t shu[16];
+    // per-row sums alternate between two buffers (MODE 1 has no fold in
+    // between); MODE 0 alternates the sum with the max, which has its own
+    __shared__ double shd[2][BT / 64];
+    __shared__ uint32_t shu[BT / 64];
     const int nch = (int)(K / 8);  // K is a multiple of 16
     const u4* gv = (const u4*)g;
     u4 w[CH], v[CH], nx[CH];
     int64_t m = blockIdx.x;
+    int parity = 0;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         const int c = threadIdx.x + j * BT;
@@ -123,7 +190,8 @@ __global__ __launch_bounds__(BT) void rmsnorm_rows_kernel(const uint16_t* __rest
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss += (double)f[e] * (double)f[e];  // exact squares
         }
-        ss = block_sum_f64(ss, shd);
+        ss = block_sum_1b<BT>(ss, shd[parity]);
+        parity ^= 1;
         const double ms = ss / (double)K;
         const double d = ms + (double)eps;
         const float r = (float)(1.0 / __builtin_sqrt(d));
@@ -150,7 +218,7 @@ __global__ __launch_bounds__(BT) void rmsnorm_rows_kernel(const uint16_t* __rest
                 if (inv_rms) inv_rms[m] = r;
             }
         } else {
-            mb = block_max_u32(mb, shu);
+            mb = block_max_1b<BT>(mb, shu);
             const float amax = __uint_as_float(mb);
             const float s = amax == 0.0f ? 1.0f : amax / 127.0f;  // IEEE division
             const double inv = 1.0 / (double)s;
@@ -175,7 +243,7 @@ __global__ __launch_bounds__(BT) void rmsnorm_rows_kernel(const uint16_t* __rest
         for (int j = 0; j < CH; ++j) v[j] = nx[j];
     }
     if constexpr (MODE == 1) {
-        block_mb = block_max_u32(block_mb, shu);
+        block_mb = block_max_1b<BT>(block_mb, shu);
         if (threadIdx.x == 0) partial[blockIdx.x] = block_mb;
     }
 }
@@ -190,7 +258,7 @@ __global__ __launch_bounds__(BT) void rmsnorm_fp8_cast_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, int64_t M, int64_t K,
     const uint32_t* __restrict__ partial, int nparts, const float* __restrict__ r_ws,
     uint8_t* __restrict__ xq, float* __restrict__ scale_out) {
-    __shared__ uint32_t shu[16];
+    __shared__ uint32_t shu[BT / 64];
     const int nch = (int)(K / 8);
     const u4* gv = (const u4*)g;
     u4 w[CH], v[CH], nx[CH];
@@ -204,7 +272,7 @@ __global__ __launch_bounds__(BT) void rmsnorm_fp8_cast_kernel(
     }
     uint32_t mb = 0;
     for (int i = threadIdx.x; i < nparts; i += BT) mb = mb > partial[i] ? mb : partial[i];
-    mb = block_max_u32(mb, shu);
+    mb = block_max_1b<BT>(mb, shu);  // the block's only fold
     const float amax = __uint_as_float(mb);
     const float s = amax == 0.0f ? 1.0f : amax / 448.0f;  // IEEE division
     const double inv = 1.0 / (double)s;
