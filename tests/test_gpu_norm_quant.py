@@ -94,10 +94,13 @@ def test_rmsnorm_fp8_llama_shapes(M, K):
 
 
 # Both block sizes (256 threads up to K = 8192, 1024 above), minimal and
-# ragged K, the largest K, both dtypes and several eps
+# ragged K, the largest K, both dtypes and several eps; more rows than the
+# persistent grid has blocks (1024 of 256 threads, 512 of 1024), so that
+# blocks walk several rows with their folds' LDS buffers alternating
 EDGE_CASES = [(1, 16, "f16", 1e-6), (3, 48, "bf16", 1e-5), (5, 8192, "bf16", 1e-5),
               (7, 8208, "f16", 1e-5), (9, 14336, "bf16", 1e-5), (4, 28672, "f16", 1e-6),
-              (2, 32768, "bf16", 1e-2), (33, 272, "f16", 0.5)]
+              (2, 32768, "bf16", 1e-2), (33, 272, "f16", 0.5), (2500, 4096, "f16", 1e-5),
+              (1100, 16384, "bf16", 1e-5)]
 
 
 @pytest.mark.parametrize("M,K,dtype,eps", EDGE_CASES)
