@@ -127,26 +127,72 @@ __device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
 }
 
 // ------------------------------------------------------------- reductions
+//
+// Wave folds use DPP lane moves inside each 16-lane row: quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  At every
+// step a lane and its partner combine the same two values, so after the
+// four steps every lane of a row holds the row's fold (max is symmetric and
+// an IEEE sum is commutative, so partners agree bit for bit).  The four
+// rows are then combined from lanes 0, 16, 32, 48 in a fixed order, giving
+// a value that is uniform over the wave, with no LDS round trip.  All 64
+// lanes must be active.
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t o = __shfl_xor(v, off, 64);
-        v = v > o ? v : o;
-    }
-    return v;
+constexpr int DPP_QP_1032 = 0xB1, DPP_QP_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,
+              DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// Max over the block, returned to every thread.  `sh` holds >= 16 words.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = umax32(v, dpp_u32<DPP_QP_1032>(v));
+    v = umax32(v, dpp_u32<DPP_QP_2301>(v));
+    v = umax32(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+    v = umax32(v, dpp_u32<DPP_ROW_MIRROR>(v));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return umax32(umax32(r0, r1), umax32(r2, r3));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64<DPP_QP_1032>(v);
+    v += dpp_f64<DPP_QP_2301>(v);
+    v += dpp_f64<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_ROW_MIRROR>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Max over the block, returned to every thread: each wave's max goes to
+// sh[wave], one barrier, then every thread folds sh in order.  `sh` holds
+// >= 16 words.  With a single barrier, two folds through the same buffer
+// need a barrier of their own between them (every caller here folds
+// through its buffer once per kernel, or alternates buffers).
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
     v = wave_max_u32(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nw = (blockDim.x + 63) >> 6;
-    __syncthreads();
-    if (lane == 0) sh[wave] = v;
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
     uint32_t m = 0;
-    for (int i = 0; i < nw; ++i) m = m > sh[i] ? m : sh[i];
+    for (int i = 0; i < nw; ++i) m = umax32(m, sh[i]);
     return m;
 }
 

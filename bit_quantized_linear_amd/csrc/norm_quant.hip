@@ -33,63 +33,12 @@
 
 namespace bql {
 
-
-// Wave folds with DPP lane moves inside each 16-lane row: quad_perm
-// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  At every
-// step a lane and its partner combine the same two values, so after the
-// four steps every lane of a row holds the row's fold (an IEEE sum is
-// commutative, so partners agree bit for bit).  The four rows are then
-// combined from lanes 0, 16, 32, 48 in a fixed order, giving a value that
-// is uniform over the wave.  No LDS round trips, unlike lane shuffles.
-constexpr int DPP_QP_1032 = 0xB1, DPP_QP_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,
-              DPP_ROW_MIRROR = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
-    return __longlong_as_double((long long)((hi << 32) | lo));
-}
-
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
-    return __longlong_as_double((long long)((hi << 32) | lo));
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-    v += dpp_f64<DPP_QP_1032>(v);
-    v += dpp_f64<DPP_QP_2301>(v);
-    v += dpp_f64<DPP_ROW_HALF_MIRROR>(v);
-    v += dpp_f64<DPP_ROW_MIRROR>(v);
-    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
-}
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
-    v = umax(v, dpp_u32<DPP_QP_1032>(v));
-    v = umax(v, dpp_u32<DPP_QP_2301>(v));
-    v = umax(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
-    v = umax(v, dpp_u32<DPP_ROW_MIRROR>(v));
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-    return umax(umax(r0, r1), umax(r2, r3));
-}
-
-// Block folds with one barrier: each wave's value goes to sh[wave], then
-// every thread folds sh[0 .. BT/64) in order.  A call's writes could race
-// with the reads of the call just before it on the same buffer, so
-// consecutive calls in a block must use different buffers (any two calls
-// further apart are separated by the barrier of the call between them).
+// Block folds with one barrier (the wave folds are device.h's DPP folds):
+// each wave's value goes to sh[wave], then every thread folds sh[0 ..
+// BT/64) in order.  A call's writes could race with the reads of the call
+// just before it on the same buffer, so consecutive calls in a block must
+// use different buffers (any two calls further apart are separated by the
+// barrier of the call between them).
 template <int BT>
 __device__ __forceinline__ double block_sum_1b(double v, double* sh) {
     v = wave_sum_f64(v);
@@ -103,12 +52,12 @@ __device__ __forceinline__ double block_sum_1b(double v, double* sh) {
 
 template <int BT>
 __device__ __forceinline__ uint32_t block_max_1b(uint32_t v, uint32_t* sh) {
-    v = wave_max_dpp(v);
+    v = wave_max_u32(v);
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < BT / 64; ++i) m = umax(m, sh[i]);
+    for (int i = 0; i < BT / 64; ++i) m = umax32(m, sh[i]);
     return m;
 }
 
