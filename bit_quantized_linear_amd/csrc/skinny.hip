@@ -7,8 +7,9 @@
 // the idle MFMA columns cost nothing that matters.
 //
 // A block of 8 waves owns one 16-row strip of A; wave w multiplies k-tiles
-// w, w + 8, ..., four in flight at a time, the first four requested before
-// the activation scale is read.  A lane's 32 operand bytes of a
+// w, w + 8, ... in batches of two, with two register sets used in turn: the
+// next batch is requested before the current one is cast and multiplied,
+// and the first batch before the activation scale is read.  A lane's 32 operand bytes of a
 // 16 x 128 tile are 32 consecutive k of one row (row = lane % 16, k =
 // 32 * (lane / 16) + 0..31, the packed layout's lane map), so A is read
 // where it is, row-major: E4M3 codes as they are, fp16 / bf16 cast to codes
@@ -21,7 +22,7 @@
 namespace bql {
 
 constexpr int SK_WAVES = 8;
-constexpr int SK_BATCH = 4;  // k-tiles a wave requests before multiplying
+constexpr int SK_BATCH = 2;  // k-tiles per register set (two sets alternate)
 constexpr int SRC_CODES = 4;
 
 // Raw loads of the lane's 32 values of A for one k-tile (row m, k0..k0+31):
@@ -86,9 +87,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
     const int64_t m = mt * TILE_N + (lane & 15);
     const int64_t kl = 32 * (lane >> 4);
     const uint8_t* wt = w + lane * 16;
-    ARaw<SRC> raw[SK_BATCH];
-    u4 bv[SK_BATCH][2];
-    auto load_batch = [&](int64_t kt0) {
+    ARaw<SRC> ra[SK_BATCH], rb[SK_BATCH];
+    u4 wa[SK_BATCH][2], wb[SK_BATCH][2];
+    auto load_batch = [&](int64_t kt0, ARaw<SRC> (&raw)[SK_BATCH], u4 (&bv)[SK_BATCH][2]) {
 #pragma unroll
         for (int u = 0; u < SK_BATCH; ++u) {
             const int64_t kt = kt0 + u * SK_WAVES;
@@ -100,8 +101,8 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
     };
     // The first batch is requested before the scale is read or folded, so
     // the scale's latency hides under it.
-    int64_t kt0 = wave;
-    load_batch(kt0);
+    constexpr int64_t STEP = SK_WAVES * SK_BATCH;
+    load_batch(wave, ra, wa);
     float sa;
     if (nparts > 0) {  // uniform: dynamic scale from the amax partials
         uint32_t mb = 0;
@@ -115,10 +116,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
     }
     const double inv = 1.0 / (double)sa;
     v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    while (true) {
-        // keep the batch's loads ahead of the casts and multiplies (the
-        // scheduler would otherwise interleave them with waits between)
-        __builtin_amdgcn_sched_barrier(0);
+    auto compute = [&](const ARaw<SRC> (&raw)[SK_BATCH], const u4 (&bv)[SK_BATCH][2]) {
 #pragma unroll
         for (int u = 0; u < SK_BATCH; ++u) {
             u4 av[2];
@@ -141,9 +139,19 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
                 }
             }
         }
-        kt0 += SK_WAVES * SK_BATCH;
-        if (kt0 >= KT) break;
-        load_batch(kt0);
+    };
+    // Two batches per trip, the sets swapping roles without copies; a batch
+    // past K reads zero A and adds nothing.  The sched barriers keep each
+    // batch's loads ahead of the casts and multiplies before them (the
+    // scheduler would otherwise sink them behind waits).
+    for (int64_t kt = wave; kt < KT; kt += 2 * STEP) {
+        load_batch(kt + STEP, rb, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ra, wa);
+        if (kt + STEP >= KT) break;  // this wave has no second batch
+        load_batch(kt + 2 * STEP, ra, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(rb, wb);
     }
     red[wave][lane] = acc;
     __syncthreads();
