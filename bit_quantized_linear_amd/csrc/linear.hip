@@ -724,8 +724,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(LinParams p) {
 // k-tile kt in registers before the barrier of iteration kt, so that
 // iteration refills slot kt % S with k-tile kt + S: S = 2 already keeps one
 // k-tile of DMA in flight behind the one being read.
+// Per-group W4A8 runs four waves of 64x64 outputs each (fewer LDS bytes per
+// MFMA than eight waves of 64x32); capped at 256 registers so that two
+// waves share a SIMD (two blocks per CU) without spilling.
 template <int V, int BM, int BN, int WM, int WN, int S>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(LinParams p) {
+__global__ __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(V == V_W4A8G ? 2 : 1, 8))) void gemm_pipe_kernel(LinParams p) {
     using C = GemmCfg<V, BM, BN, WM, WN, S>;
     using Acc = typename VT<V>::Acc;
     constexpr int NW = C::NW, FM = C::FM, FN = C::FN, BT = C::BT;
@@ -1285,7 +1289,9 @@ static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
         if (t128 <= CUS) return launch_gemm_pipe<V, 128, 128, 4, 2, 3>(p, stream);
         if (t256 >= 3 * CUS / 2) return launch_gemm<V, 256, 256, 4, 4, 2>(p, stream);
         return launch_gemm<V, 128, 128, 2, 4, 2>(p, stream);
-    } else {  // W4A8 (and its per-group form): best at every K = N in 4096..8192 measured
+    } else if constexpr (V == V_W4A8G) {  // best at every K = N in 4096..8192 measured
+        return launch_gemm_pipe<V, 128, 128, 2, 2, 2>(p, stream);
+    } else {  // per-channel W4A8: best at every K = N in 4096..8192 measured
         return launch_gemm_pipe<V, 128, 128, 2, 4, 2>(p, stream);
     }
 }
