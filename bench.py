@@ -15,7 +15,7 @@ small-M kernel with its split-K reduce) is timed the same way and reported
 in HBM GB/s of algorithmic bytes.  Weights rotate over enough copies that
 each pass touches more than twice the 256 MB Infinity Cache.
 
-Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus above 1 is refused: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -124,9 +124,9 @@ def summarize_traffic(fetch_dir, write_dir):
     text = ["# HBM traffic of the dominant GEMM launches, M=1024 N=28672 K=4096",
             "# (tiled GEMM, exact = f16 MFMA on decoded fp8, fast = fp8 MFMA; pre-quantized A)",
             "commands (repo root; cd /tmp && export TMPDIR=/tmp first, then back):",
-            "  rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --roofline-only",
-            "  rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python3 bench.py --roofline-only",
-            "  python3 bench.py --summarize-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+            f"  rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python3 bench.py --roofline-only",
+            f"  rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o run -- python3 bench.py --roofline-only",
+            f"  python3 bench.py --summarize-traffic {fetch_dir} {write_dir}",
             f"source_sha256: {kernel_source_hash()}",
             "details:"] + lines + [
             f"  algorithmic bytes per launch (Aq + Wq + bf16 Y + scales): {alg}",
@@ -163,8 +163,8 @@ def summarize_mfma(pmc_dir):
              "# (tiled GEMM, pre-quantized A; exact = f16 MFMA on decoded fp8, fast = fp8 MFMA)",
              "commands (repo root; cd /tmp && export TMPDIR=/tmp first, then back):",
              "  rocprofv3 --pmc " + " ".join(MFMA_COUNTERS)
-             + " -f csv -d gpurun_out/pmc_mfma -o run -- python3 bench.py --roofline-only",
-             "  python3 bench.py --summarize-mfma gpurun_out/pmc_mfma",
+             + f" -f csv -d {pmc_dir} -o run -- python3 bench.py --roofline-only",
+             f"  python3 bench.py --summarize-mfma {pmc_dir}",
              f"source_sha256: {kernel_source_hash()}",
              f"algorithmic flops per launch (2*M*N*K): {flops}"]
     for tag, sig, mops in (("exact", "gemm_kernel<3,", "SQ_INSTS_VALU_MFMA_MOPS_F16"),
@@ -594,7 +594,7 @@ def main():
         summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
