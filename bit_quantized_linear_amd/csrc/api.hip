@@ -360,8 +360,9 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
         return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
     }
     const float* sa = a_scale;
-    // pre-quantized A on the small-M path is read row-major where it is
-    const bool direct = adt == BQL_E4M3 && bql::use_small_m(variant, M, N, K);
+    // pre-quantized A is read row-major where it is by the kernels that read
+    // it that way at full speed (small M, the k-split exact tile kernel)
+    const bool direct = adt == BQL_E4M3 && bql::reads_rowmajor_a(variant, M, N, K);
     hipError_t e = hipSuccess;
     if (adt != BQL_E4M3) {
         e = bql::launch_quant_dynamic_packed(a, adt, M, K, aq, a_scale, wsb, s);

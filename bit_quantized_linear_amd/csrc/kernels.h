@@ -97,7 +97,8 @@ struct LinearArgs {
     int xdt = 0;
     float* scale_out = nullptr;  // optional copy of sA for the caller
     float* scale_ws = nullptr;   // sA in the workspace (read by the split-K reduce)
-    // small-M path only: 8-bit A is read row-major [M, K] (no repack launch)
+    // 8-bit A is read row-major [M, K] where it is (no repack launch); only
+    // where reads_rowmajor_a() holds
     int a_rowmajor = 0;
     // fused small-M fp8 with a static activation scale (no amax): sA = *given_scale
     const float* given_scale = nullptr;
@@ -110,6 +111,10 @@ bool fused_small_m(int64_t M, int64_t N, int64_t K);
 size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant);
 // Which path runs: true for the streaming small-M kernels.
 bool use_small_m(int variant, int64_t M, int64_t N, int64_t K);
+// Whether the kernel that runs at this shape reads 8-bit A row-major at full
+// speed: the small-M kernels and the k-split exact tile kernel.  The other
+// tile kernels are faster on packed operand tiles even with the repack.
+bool reads_rowmajor_a(int variant, int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace bql

@@ -548,6 +548,48 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t nbm, int64_t nbn,
     bn = rem / gm;
 }
 
+// The A operand of the k-split tile kernel: a block's BM rows of A, either packed
+// into 16x128 operand tiles (2 KiB each, [16-row strip][k-tile]) or
+// row-major [M,K] bytes (E4M3 codes or int8) where the caller keeps them.
+// Both give the same LDS image: the 16-byte load of (strip s, half h) by
+// lane l holds row 16 s + l % 16 and k = 128 kt + 32 (l / 16) + 16 h ..
+// +15 of the block's rows (the packed layout stores exactly that there).
+// Rows past M lie past the descriptor's range and chunks past K (a multiple
+// of 16) get an offset past it, so both read as zero.
+struct ATiles {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int KT;
+    int K;
+    bool rowmajor;
+};
+
+template <int BM>
+__device__ __forceinline__ ATiles a_tiles(const LinParams& p, int64_t m0) {
+    ATiles t;
+    t.KT = (int)p.KT;
+    t.K = (int)p.K;
+    t.rowmajor = p.a_rowmajor != 0;
+    if (t.rowmajor) {
+        const int64_t rows = p.M - m0 < BM ? p.M - m0 : BM;  // <= 256 rows of K <= 2^22 bytes
+        t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.a + m0 * p.K), (short)0,
+                                                   (int)(rows * p.K), 0x00020000);
+    } else {
+        const int64_t mt0 = m0 / 16, mtiles = (p.M + 15) / 16;
+        const int64_t strips = mtiles - mt0 < BM / 16 ? mtiles - mt0 : BM / 16;
+        t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.a + mt0 * p.KT * 2048),
+                                                   (short)0, (int)(strips * p.KT * 2048), 0x00020000);
+    }
+    return t;
+}
+
+__device__ __forceinline__ int a_tile_offset(const ATiles& t, int strip, int h, int kt, int lane) {
+    if (t.rowmajor) {
+        const int k = kt * 128 + 32 * (lane >> 4) + 16 * h;
+        return k < t.K ? (strip * 16 + (lane & 15)) * t.K + k : 0x7FFFFFF0;
+    }
+    return (strip * t.KT + kt) * 2048 + h * 1024 + lane * 16;
+}
+
 template <int V, int BM, int BN, int WM, int WN, int S>
 struct GemmCfg {
     static constexpr int NW = WM * WN;
@@ -962,15 +1004,12 @@ __global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
     int64_t bm, bn;
     tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, bm, bn);
     const int64_t m0 = bm * BM, n0 = bn * BN;
-    const int64_t mt0 = m0 / 16, nt0 = n0 / 16;
-    const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
+    const int64_t nt0 = n0 / 16, ntiles = p.N / 16;
     const int KT = (int)p.KT;
 
-    const int64_t a_strips = mtiles - mt0 < BM / 16 ? mtiles - mt0 : BM / 16;
+    // A packed or row-major (see ATiles)
     const int64_t b_strips = ntiles - nt0 < BN / 16 ? ntiles - nt0 : BN / 16;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)p.a + mt0 * p.KT * 2048), (short)0, (int)(a_strips * p.KT * 2048),
-        0x00020000);
+    const ATiles at = a_tiles<BM>(p, m0);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.w + nt0 * p.KT * 2048), (short)0, (int)(b_strips * p.KT * 2048), 0x00020000);
 
@@ -979,9 +1018,9 @@ __global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
 #pragma unroll
         for (int i = 0; i < C::A_LD / NW; ++i) {
             const int slot = wave + NW * i;
-            const int off = ((slot >> 1) * KT + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + slot * 1024), 16, off, 0,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(at.rsrc, (lds_ptr_t)(base + slot * 1024), 16,
+                                                     a_tile_offset(at, slot >> 1, slot & 1, kt, lane),
+                                                     0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < C::B_LD / NW; ++i) {
@@ -1271,12 +1310,25 @@ static hipError_t launch_gemm_ks(const LinParams& p, hipStream_t stream) {
 // k-split exact kernel and the register-prefetching fp8 kernel with a
 // three-stage ring; shapes with many 256x256 tiles favour the big fp8 tile.
 constexpr int64_t CUS = 256;
+// Exact fp8 with at most one 128x128 output tile per CU runs the k-split kernel.
+static bool uses_ks(int variant, int64_t M, int64_t N) {
+    return variant == V_FP8X && ((M + 127) / 128) * ((N + 127) / 128) <= CUS;
+}
+
+// Row-major 8-bit A (per-lane gathers of 16-byte chunks from 16 rows)
+// costs the tile kernels that re-read A from L2 for many column tiles more
+// than a repack launch: at M = 1024, +3 % for the exact 128x128 kernel at
+// N = 28672 and +37 % for W4A8, against -5 to -9 % for the k-split kernel.
+bool reads_rowmajor_a(int variant, int64_t M, int64_t N, int64_t K) {
+    return use_small_m(variant, M, N, K) || uses_ks(variant, M, N);
+}
+
 template <int V>
 static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
     const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
     if constexpr (V == V_FP8X) {
-        if (t128 <= CUS) return launch_gemm_ks<128, 128, 2, 2, 2>(p, stream);
+        if (uses_ks(V, p.M, p.N)) return launch_gemm_ks<128, 128, 2, 2, 2>(p, stream);
         // Two blocks share a CU, so the busiest CU carries ceil(tiles / CUs)
         // tiles: 128x96 tiles win where they even that out (M = 1024, N =
         // 6144: 384 tiles of 128 columns leave half the CUs with two, 512
@@ -1336,7 +1388,8 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
             default: return run_gemv<V_W4A8, false>(p, stream);
         }
     }
-    if (args.a_rowmajor) return hipErrorInvalidValue;  // the tile kernels read packed A only
+    if (args.a_rowmajor && !reads_rowmajor_a(args.variant, args.M, args.N, args.K))
+        return hipErrorInvalidValue;  // this shape's tile kernel takes packed A
     p.KT = (args.K + TILE_K - 1) / TILE_K;
     p.kt_per_split = p.KT;
     p.splits = 1;

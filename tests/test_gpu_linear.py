@@ -315,6 +315,25 @@ def test_prequantized_input_and_scale_interleave(M):
     assert_close(host_f64(y_c), y_ref, f"pre-quantized M={M}")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 1040, 400), (2064, 2192, 400)])
+def test_prequantized_rowmajor_and_packed_tile_paths(M, N, K):
+    # E4M3 A at M > 16 in exact mode: up to 256 output tiles of 128x128 the
+    # k-split kernel gathers A row-major where it is, above that A is first
+    # repacked into operand tiles; ragged M and K (K = 3 * 128 + 16) on both.
+    g = np.random.Generator(np.random.PCG64(M + N))
+    aq = _random_codes(g, (M, K))
+    wq = _random_codes(g, (N, K))
+    sa = np.float32(0.011)
+    sw = (g.uniform(0.5, 2.0, size=N) * 2.0 ** -6).astype(np.float32)
+    pw = bql.prepack_weight(dev(wq), "fp8_channel", scales=dev(sw))
+    y = bql.fp8_linear(dev(aq).view(torch.float8_e4m3fn), pw, a_scale=torch.tensor([sa], device=DEV),
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = rows_for(M, 7 + M, 40)
+    assert_close(host_f64(y)[rows], oracle.fp8_linear(aq, sa, wq, sw, rows=rows),
+                 f"pre-quantized tile path M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M", [1, 3, 16])
 def test_prequantized_small_m_half_tiles(M):
     # Pre-quantized A on the small-M path is read row-major; K = 144 leaves
