@@ -1,0 +1,92 @@
+"""GPU parity at the largest reductions the linears accept, against the CPU
+oracle.
+
+fp8 linear at K = 2^22 (the bql_fp8_linear limit), N = 16: the small-M
+path with fused dynamic quantization (M = 1), the tile path with dynamic
+quantization and with pre-quantized E4M3 A (M = 40).  W4A8 at K = 131072
+(the limit that keeps 16 * acc inside int32), int32 accumulators compared
+bit for bit, with every product at its largest magnitude of one sign so
+that the sum reaches its extreme.  Per-group W4A8 at K = 16384 (128 groups,
+the limit of the staged scales).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from _common import DEV, assert_close, dev, dev16, host, host_f64, say
+
+import bit_quantized_linear_amd as bql
+
+pytestmark = pytest.mark.gpu
+
+K_FP8 = 1 << 22
+K_W4A8 = 131072
+K_GROUP = 16384
+
+
+@pytest.fixture(scope="module")
+def fp8_case():
+    g = wl.rng(120, 0)
+    N = 16
+    wb = wl.weight(g, N, K_FP8, "bf16")
+    ab = wl.activation(g, 40, K_FP8, "bf16", "channels")
+    wq, sw = oracle.quant_per_tensor(oracle.decode_input(wb, "bf16"))
+    pw = bql.prepack_weight(dev16(wb, "bf16"), "fp8_tensor")
+    return wb, ab, wq, sw, pw
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_fp8_linear_max_k_dynamic(fp8_case, M):
+    _, ab, wq, sw, pw = fp8_case
+    sa = torch.empty(1, dtype=torch.float32, device=DEV)
+    y = bql.fp8_linear(dev16(ab[:M], "bf16"), pw, a_scale=sa, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    aq, sa_ref = oracle.quant_per_tensor(oracle.decode_input(ab[:M], "bf16"))
+    assert sa.item() == float(sa_ref), "activation scale differs"
+    assert_close(host_f64(y), oracle.fp8_linear(aq, sa_ref, wq, sw), f"fp8 K=2^22 M={M}")
+    say(f"  fp8 linear M={M} N=16 K=2^22 within tolerance")
+
+
+def test_fp8_linear_max_k_prequantized(fp8_case):
+    _, ab, wq, sw, pw = fp8_case
+    aq, sa = oracle.quant_per_tensor(oracle.decode_input(ab, "bf16"))
+    y = bql.fp8_linear(dev(aq).view(torch.float8_e4m3fn), pw, a_scale=torch.tensor([sa], device=DEV),
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(host_f64(y), oracle.fp8_linear(aq, sa, wq, sw), "fp8 K=2^22 M=40 E4M3 A")
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_w4a8_max_k_extreme_sum(M):
+    # most products are -127 * -8 = +1016: a row with all of them would give
+    # acc = 1016 * K, i.e. 16 * acc = 2^31 - 2^24, the top of the int32 range
+    # the int8 MMA works in; a few sign changes make the rows differ
+    N = 16
+    w4 = np.full((N, K_W4A8), -8, dtype=np.int8)
+    aq = np.full((M, K_W4A8), -127, dtype=np.int8)
+    aq[:, ::7] = 127
+    w4[1::2, ::5] = 7
+    pw = bql.prepack_weight(torch.from_numpy(wl.pack_int4(w4).reshape(N, K_W4A8 // 2)).to(DEV),
+                            "int4_channel", scales=torch.ones(N, dtype=torch.float16, device=DEV))
+    acc = bql.w4a8_linear(dev(aq), None, pw, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    ref = oracle.w4a8_acc(aq, w4)
+    assert np.abs(ref).max() < 2 ** 31 // 16, "the case must stay inside the documented range"
+    assert np.array_equal(host(acc).astype(np.int64), ref), f"W4A8 K={K_W4A8} M={M} accumulators differ"
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_w4a8_group_max_k(M):
+    N = 32
+    g = wl.rng(121, M)
+    w4 = wl.int4_weight(g, N, K_GROUP)
+    sw = (g.uniform(0.5, 2.0, size=(N, K_GROUP // 128)) * 2.0 ** -8).astype(np.float32)
+    pw = bql.prepack_weight(torch.from_numpy(wl.pack_int4(w4).reshape(N, K_GROUP // 2)).to(DEV),
+                            "int4_group", scales=dev(sw))
+    aq = g.integers(-127, 128, size=(M, K_GROUP), dtype=np.int8)
+    sa = g.uniform(1e-3, 1e-1, size=M).astype(np.float32)
+    y = bql.w4a8_group_linear(dev(aq), dev(sa), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(host_f64(y), oracle.w4a8_group_linear(aq, sa, w4, sw), f"g128 K={K_GROUP} M={M}")
