@@ -7,7 +7,8 @@ quantization and with pre-quantized E4M3 A (M = 40).  W4A8 at K = 131072
 (the limit that keeps 16 * acc inside int32), int32 accumulators compared
 bit for bit, with every product at its largest magnitude of one sign so
 that the sum reaches its extreme.  Per-group W4A8 at K = 16384 (128 groups,
-the limit of the staged scales).
+the limit of the staged scales).  W8A16 at K = 2^24, the limit of the
+weight formats.
 """
 import numpy as np
 import pytest
@@ -90,3 +91,20 @@ def test_w4a8_group_max_k(M):
     y = bql.w4a8_group_linear(dev(aq), dev(sa), pw, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(host_f64(y), oracle.w4a8_group_linear(aq, sa, w4, sw), f"g128 K={K_GROUP} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_w8a16_max_k(M):
+    # K = 2^24, the limit of the weight formats; per-channel fp16 scales
+    N, K = 16, 1 << 24
+    g = wl.rng(122, M)
+    wb = wl.weight(g, N, K, "f16")
+    wf = oracle.decode_input(wb, "f16")
+    sbits = wl.w8a16_channel_scales(g, wf)
+    s32 = oracle.decode_input(sbits, "f16")
+    pw = bql.prepack_weight(dev16(wb, "f16"), "fp8_channel", scales=dev16(sbits, "f16"))
+    ab = wl.activation(g, M, K, "f16")
+    y = bql.w8a16_linear(dev16(ab, "f16"), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.w8a16_linear(oracle.decode_input(ab, "f16"), oracle.quant_with_scales(wf, s32), s32)
+    assert_close(host_f64(y), ref, f"W8A16 K=2^24 M={M}")
