@@ -8,7 +8,7 @@ quantization and with pre-quantized E4M3 A (M = 40).  W4A8 at K = 131072
 bit for bit, with every product at its largest magnitude of one sign so
 that the sum reaches its extreme.  Per-group W4A8 at K = 16384 (128 groups,
 the limit of the staged scales).  W8A16 at K = 2^24, the limit of the
-weight formats.
+weight formats.  Both RMSNorm quantizers at M = 2^22, the row limit.
 """
 import numpy as np
 import pytest
@@ -108,3 +108,26 @@ def test_w8a16_max_k(M):
     torch.cuda.synchronize()
     ref = oracle.w8a16_linear(oracle.decode_input(ab, "f16"), oracle.quant_with_scales(wf, s32), s32)
     assert_close(host_f64(y), ref, f"W8A16 K=2^24 M={M}")
+
+
+def test_rmsnorm_quantizers_max_m():
+    # M = 2^22 (the row limit) with K = 32: every block of the persistent
+    # grid walks about 4096 rows, and the E4M3 cast folds 1024 block maxima
+    M, K = 1 << 22, 32
+    g = wl.rng(123, 0)
+    xb = wl.activation(g, M, K, "f16", "entries")
+    gb = wl.norm_weight(g, K, "f16")
+    x = oracle.decode_input(xb, "f16")
+    gf = oracle.decode_input(gb, "f16")
+    lo, hi = oracle.rms_inv_candidates(x, 1e-5)
+    q8, s8, r8 = bql.rmsnorm_int8_quantize_per_token(dev16(xb, "f16"), dev16(gb, "f16"), 1e-5, inv_rms=True)
+    qf, sf, rf = bql.rmsnorm_fp8_quantize_dynamic(dev16(xb, "f16"), dev16(gb, "f16"), 1e-5, inv_rms=True)
+    torch.cuda.synchronize()
+    for r in (host(r8), host(rf)):
+        assert ((r == lo) | (r == hi)).all(), "inadmissible 1/rms"
+    q_ref, s_ref, _ = oracle.rmsnorm_int8_per_token(x, gf, 1e-5, r=host(r8))
+    assert np.array_equal(host(s8).view(np.uint32), s_ref.view(np.uint32)), "int8 scales differ"
+    assert np.array_equal(host(q8), q_ref), "int8 codes differ"
+    qf_ref, sf_ref, _ = oracle.rmsnorm_fp8_per_tensor(x, gf, 1e-5, r=host(rf))
+    assert host(sf).view(np.uint32)[0] == np.float32(sf_ref).view(np.uint32), "E4M3 scale differs"
+    assert np.array_equal(host(qf), qf_ref), "E4M3 codes differ"
