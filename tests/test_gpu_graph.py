@@ -2,7 +2,8 @@
 
 Every path is captured once (small-M fused and split-K, the tiled kernel,
 exact and fast accumulation, W8A16, W4A8, the static-scale linear, the
-small-N linear, the fused RMSNorm quantizers, per-group W4A8) and replayed
+small-N linear, the fused RMSNorm quantizers, per-group W4A8, pre-quantized
+A read row-major by the k-split kernel) and replayed
 several times with eager work and synchronizations in between; each replay
 must equal the eager output bit for bit (all kernels are deterministic).
 """
@@ -143,3 +144,20 @@ def test_w4a8_group_graph(M):
                      device=DEV)
     _replays_match(lambda: bql.w4a8_group_linear(aq, sa, pw, out=out, ws=ws), out,
                    lambda: bql.w4a8_group_linear(aq, sa * 2, pw))
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 1024, 1040), (64, 272, 400)])
+def test_prequantized_ksplit_graph(M, N, K):
+    # E4M3 A at M > 16 with few output tiles: the k-split kernel gathers A
+    # row-major where it is (no repack launch); ragged K
+    g = np.random.Generator(np.random.PCG64(M + K))
+    codes = g.integers(0, 256, (M, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    pw = bql.prepack_weight(dev16(wl.weight(wl.rng(17, N), N, K, "bf16"), "bf16"), "fp8_channel")
+    a = dev(codes).view(torch.float8_e4m3fn)
+    sa = torch.tensor([0.02], dtype=torch.float32, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=DEV)
+    other = torch.empty_like(out)
+    _replays_match(lambda: bql.fp8_linear(a, pw, a_scale=sa, out_dtype=torch.bfloat16, out=out, ws=ws),
+                   out, lambda: bql.fp8_linear(a, pw, a_scale=sa * 2, out_dtype=torch.bfloat16, out=other))
