@@ -25,6 +25,12 @@
  *  - output_scale: an optional FP8 egress of a layer, quantized with a
  *    given output scale (vLLM FP8 quantization-schema RFC, the answer on
  *    output_scale).
+ *  - RMSNorm followed by either activation quantizer (QQQ issue #15, the
+ *    answer on online activation quantization fused into rmsnorm), with the
+ *    precision reading stated at bqo_rmsnorm below.
+ *  - Per-group W4A8, one scale per output channel and 128-k group (QQQ
+ *    issue #15, the "qqq-g128" columns), with the reading stated at
+ *    bqo_w4a8_group_linear below.
  *
  * Readings where the pages are silent are ours and are listed in the design
  * notes: RNE, saturation to +-448, sign kept on zero/underflow, IEEE fp32
