@@ -143,20 +143,33 @@ def test_quant_worked_examples():
     n = 0
     for tok in _golden_lines("quant_worked.txt"):
         line = " ".join(tok[1:])
-        ins, scale, outs = [p.split() for p in line.split("|")]
+        parts = [p.split() for p in line.split("|")]
+        ins, scale, outs = parts[-3:]
         if tok[0] == "quant":
             dtype, vals = ins[0], np.array([float(t) for t in ins[1:]], dtype=np.float32)
             x = oracle.decode_input(wl.to_bits(vals, dtype), dtype) if dtype != "f32" else vals
             q, s = oracle.quant_per_tensor(x)
             assert s == np.float32(float(scale[0]))
             assert list(q) == [int(c, 16) for c in outs]
+        elif tok[0] in ("perrow", "withscales"):
+            dtype, cols = tok[1], int(tok[2])
+            vals = np.array([float(t) for t in ins], dtype=np.float32)
+            x = oracle.decode_input(wl.to_bits(vals, dtype), dtype) if dtype != "f32" else vals
+            x = x.reshape(-1, cols)
+            sc = np.array([float(t) for t in scale], dtype=np.float32)
+            if tok[0] == "perrow":
+                q, s = oracle.quant_per_row(x)
+                assert np.array_equal(s, sc)
+            else:
+                q = oracle.quant_with_scales(x, sc)
+            assert list(q.ravel()) == [int(c, 16) for c in outs]
         else:
             x = np.array([[float(t) for t in ins]], dtype=np.float32)
             q, s = oracle.int8_quant_per_token(x)
             assert s[0] == np.float32(float(scale[0]))
             assert list(q[0]) == [int(c) for c in outs]
         n += 1
-    assert n == 6
+    assert n == 8
 
 
 def _sample(seed, M=8, K=256):
@@ -210,6 +223,54 @@ def test_per_row_with_equal_rows_equals_per_tensor():
     assert np.all(sr == st)
     assert np.array_equal(qt, qr)
     assert np.array_equal(oracle.quant_with_scales(x, np.array([st])), qt)
+
+
+def _rows_scaled_by_row_index(seed, rows=16, cols=96):
+    """Rows n = base * 2^(n mod 8) (exact in fp32): every row has the same
+    codes and row n's scale is exactly 2^(n mod 8) times row 0's."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    base = (g.standard_normal(cols) * np.where(g.random(cols) < 0.05, 20, 1)).astype(np.float32)
+    mult = np.exp2(np.arange(rows) % 8).astype(np.float32)
+    return (base[None, :] * mult[:, None]).astype(np.float32), mult
+
+
+def test_per_row_quant_uses_each_rows_own_amax():
+    # a global amax, or the amax of another row, gives other codes for all
+    # but one of these rows
+    x, mult = _rows_scaled_by_row_index(21)
+    q, s = oracle.quant_per_row(x)
+    for n in range(x.shape[0]):
+        assert np.array_equal(q[n], q[0]), n
+        assert s[n] == np.float32(s[0] * mult[n]), n
+    # and each row is quantized exactly as the (hand-pinned) per-tensor
+    # quantizer quantizes that row alone
+    g = np.random.Generator(np.random.PCG64(22))
+    y = (g.standard_normal((12, 80)) * np.exp2(g.integers(-6, 7, (12, 1)))).astype(np.float32)
+    y[5] = 0.0  # an all-zero row takes scale 1
+    q, s = oracle.quant_per_row(y)
+    for n in range(y.shape[0]):
+        qn, sn = oracle.quant_per_tensor(y[n])
+        assert np.array_equal(q[n], qn) and s[n] == sn, n
+    assert s[5] == np.float32(1.0) and not q[5].any()
+
+
+def test_quant_with_scales_applies_each_rows_scale():
+    # position-revealing scales: row n divided by its own 2^(n mod 8) * s0
+    # gives row 0's codes on every row; any other row's scale does not
+    x, mult = _rows_scaled_by_row_index(23)
+    q0, s0 = oracle.quant_per_tensor(x[0])
+    sc = (s0 * mult).astype(np.float32)
+    q = oracle.quant_with_scales(x, sc)
+    for n in range(x.shape[0]):
+        assert np.array_equal(q[n], q0), n
+    # the scales the per-row quantizer chose, given back, give its codes
+    g = np.random.Generator(np.random.PCG64(24))
+    y = (g.standard_normal((9, 64)) * np.exp2(g.integers(-4, 5, (9, 1)))).astype(np.float32)
+    qr, sr = oracle.quant_per_row(y)
+    assert np.array_equal(oracle.quant_with_scales(y, sr), qr)
+    # and one scale for the whole matrix is the per-tensor quantizer
+    qt, st = oracle.quant_per_tensor(y)
+    assert np.array_equal(oracle.quant_with_scales(y, np.array([st], np.float32)), qt)
 
 
 def test_int8_per_token_invariants():
