@@ -17,6 +17,7 @@ Operations (see the header for the exact contracts):
   unpack_weight           logical codes back from the packed layout
   fp8_linear              Y = (sA sW[n]) (Aq Wq^T), fp16/bf16/E4M3 output
   fp8_linear_static       the same with a given (static) activation scale
+  fp8_linear_noalloc      fp8_linear on the library's own scratch (no workspace)
   w8a16_linear            Y = sW[n] (A Wq^T), fp16 activations
   w4a8_linear             int4 x int8 with int32 accumulation
   w4a8_group_linear       the same with a scale per channel and 128-k group
@@ -76,6 +77,7 @@ SIGNATURES = {
     "bql_fp8_linear": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ, _P]),
     "bql_fp8_linear_static": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _I, _I, _P, _SZ,
                                    _P]),
+    "bql_fp8_linear_noalloc": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _I, _I, _P]),
     "bql_w8a16_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "bql_w8a16_linear": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "bql_w4a8_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
@@ -320,6 +322,32 @@ def fp8_linear_static(a: torch.Tensor, pw: PackedWeight, a_scale: torch.Tensor,
                                    _ptr(pw.scales), int(pw.per_channel), M, N, K,
                                    _ptr(output_scale), _ptr(out), ydt, int(bool(fast_accum)),
                                    _ptr(ws), nb, _stream(a.device)))
+    return out
+
+
+# scratch the library holds for fp8_linear_noalloc (BQL_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fp8_linear_noalloc(a: torch.Tensor, pw: PackedWeight, a_scale: Optional[torch.Tensor] = None,
+                       out_dtype: torch.dtype = torch.bfloat16,
+                       output_scale: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, fast_accum: bool = False) -> torch.Tensor:
+    """fp8_linear on the library's own per-GPU scratch: no workspace argument
+    and no allocation inside the call (`out` may be given so that the call
+    allocates nothing at all).  Calls overlapping on one GPU race."""
+    _need_cuda(a, a_scale, output_scale, out)
+    L = lib()
+    M, K = a.shape
+    N = pw.N
+    ydt = _TORCH_TO_BQL[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.uint8 if ydt == E4M3 else out_dtype, device=a.device)
+    _check("bql_fp8_linear_noalloc",
+           L.bql_fp8_linear_noalloc(_ptr(a), _TORCH_TO_BQL[a.dtype], _ptr(a_scale), _ptr(pw.packed),
+                                    _ptr(pw.scales), int(pw.per_channel), M, N, K,
+                                    _ptr(output_scale), _ptr(out), ydt, int(bool(fast_accum)),
+                                    _stream(a.device)))
     return out
 
 

@@ -6,9 +6,19 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "bql.h"
 #include "kernels.h"
 #include "skinny.h"
+
+// Scratch of bql_fp8_linear_noalloc: device memory that the library
+// itself holds, one copy per GPU (each device's code object has its own),
+// kept until the process ends.  In host code `scratch` is a stand-in, not a
+// device address: kernels and copies get the address that
+// hipGetSymbolAddress returns on that device.
+static __device__ __align__(256) uint8_t scratch[BQL_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -91,6 +101,33 @@ bql_status hip_status(hipError_t e) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t ktiles(int64_t K) { return (K + 127) / 128; }
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_ptr[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// The address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+bql_status device_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(BQL_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(BQL_ERR_ARG, "device %d beyond %d devices", dev, MAX_DEVICES);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(BQL_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                            hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BQL_OK;
+}
 
 }  // namespace
 
@@ -308,11 +345,12 @@ static bql_status skinny_fp8_linear(const void* a, bql_dtype adt, const float* a
                                                 accum == BQL_ACCUM_FAST, s));
 }
 
-bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const void* w_packed,
-                          const float* w_scale, int w_per_channel, int64_t M, int64_t N, int64_t K,
-                          const float* output_scale, void* y, bql_dtype ydt, bql_accum accum,
-                          void* ws, size_t ws_bytes, bql_stream stream) {
-    hipStream_t s = (hipStream_t)stream;
+// Argument checks of bql_fp8_linear and bql_fp8_linear_noalloc, all but the
+// workspace.
+static bql_status check_fp8_linear(const void* a, bql_dtype adt, const float* a_scale,
+                                   const void* w_packed, const float* w_scale, int w_per_channel,
+                                   int64_t M, int64_t N, int64_t K, const float* output_scale,
+                                   const void* y, bql_dtype ydt, bql_accum accum) {
     CHECK(need_m(M));
     CHECK(need_nk_fp8(N, K));
     if (K > (int64_t(1) << 22)) return fail(BQL_ERR_SHAPE, "K above 2^22");
@@ -321,7 +359,7 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
         return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16, BQL_F32 or BQL_E4M3");
     if (w_per_channel != 0 && w_per_channel != 1) return fail(BQL_ERR_ARG, "w_per_channel must be 0 or 1");
     if (accum != BQL_ACCUM_EXACT && accum != BQL_ACCUM_FAST) return fail(BQL_ERR_ARG, "unknown accum %d", (int)accum);
-    if (M == 0) return ok();
+    if (M == 0) return BQL_OK;
     CHECK(need_ptr(a, "a"));
     CHECK(need_ptr(w_packed, "w_packed"));
     CHECK(need_scalar(w_scale, "w_scale"));
@@ -329,8 +367,15 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     if (adt == BQL_E4M3) CHECK(need_scalar(a_scale, "a_scale"));
     else if (a_scale && (((uintptr_t)a_scale) & 3u)) return fail(BQL_ERR_ALIGN, "a_scale misaligned");
     if (ydt == BQL_E4M3) CHECK(need_scalar(output_scale, "output_scale"));
-    CHECK(need_ws(ws, ws_bytes, bql_fp8_linear_workspace_size(M, N, K)));
+    return BQL_OK;
+}
 
+// The launches of bql_fp8_linear on checked arguments, M > 0, with a
+// workspace of at least bql_fp8_linear_workspace_size(M, N, K) bytes.
+static bql_status run_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const void* w_packed,
+                                 const float* w_scale, int w_per_channel, int64_t M, int64_t N,
+                                 int64_t K, const float* output_scale, void* y, bql_dtype ydt,
+                                 bql_accum accum, void* ws, hipStream_t s) {
     if (N <= bql::SKINNY_MAX_N)
         return skinny_fp8_linear(a, adt, a_scale, a_scale, false, w_packed, w_scale, w_per_channel,
                                  M, N, K, output_scale, y, ydt, accum, ws, s);
@@ -386,6 +431,37 @@ bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const vo
     la.w_per_channel = w_per_channel;
     la.out_scale = output_scale;
     return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+}
+
+bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const void* w_packed,
+                          const float* w_scale, int w_per_channel, int64_t M, int64_t N, int64_t K,
+                          const float* output_scale, void* y, bql_dtype ydt, bql_accum accum,
+                          void* ws, size_t ws_bytes, bql_stream stream) {
+    CHECK(check_fp8_linear(a, adt, a_scale, w_packed, w_scale, w_per_channel, M, N, K, output_scale,
+                           y, ydt, accum));
+    if (M == 0) return ok();
+    CHECK(need_ws(ws, ws_bytes, bql_fp8_linear_workspace_size(M, N, K)));
+    return run_fp8_linear(a, adt, a_scale, w_packed, w_scale, w_per_channel, M, N, K, output_scale,
+                          y, ydt, accum, ws, (hipStream_t)stream);
+}
+
+bql_status bql_fp8_linear_noalloc(const void* a, bql_dtype adt, float* a_scale,
+                                  const void* w_packed, const float* w_scale, int w_per_channel,
+                                  int64_t M, int64_t N, int64_t K, const float* output_scale,
+                                  void* y, bql_dtype ydt, bql_accum accum, bql_stream stream) {
+    CHECK(check_fp8_linear(a, adt, a_scale, w_packed, w_scale, w_per_channel, M, N, K, output_scale,
+                           y, ydt, accum));
+    if (M == 0) return ok();
+    const size_t need = bql_fp8_linear_workspace_size(M, N, K);
+    if (need > BQL_NOALLOC_SCRATCH_BYTES)
+        return fail(BQL_ERR_SHAPE,
+                    "M=%lld N=%lld K=%lld needs %zu bytes of scratch, above the %zu bytes of "
+                    "bql_fp8_linear_noalloc (use bql_fp8_linear with a workspace)",
+                    (long long)M, (long long)N, (long long)K, need, (size_t)BQL_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    CHECK(device_scratch(&ws));
+    return run_fp8_linear(a, adt, a_scale, w_packed, w_scale, w_per_channel, M, N, K, output_scale,
+                          y, ydt, accum, ws, (hipStream_t)stream);
 }
 
 bql_status bql_fp8_linear_static(const void* a, bql_dtype adt, const float* a_scale,

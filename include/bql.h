@@ -277,6 +277,25 @@ bql_status bql_fp8_linear_static(const void* a, bql_dtype adt, const float* a_sc
                                  void* y, bql_dtype ydt, bql_accum accum, void* ws,
                                  size_t ws_bytes, bql_stream stream);
 
+/* Allocation-free bql_fp8_linear, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and
+ * errors as bql_fp8_linear without ws / ws_bytes: the kernels' scratch (the
+ * amax partials and scale, the packed activation codes, split-K partials)
+ * is a BQL_NOALLOC_SCRATCH_BYTES array the library holds in device memory,
+ * one per GPU, kept until the process ends.  Calls whose
+ * bql_fp8_linear_workspace_size(M, N, K) exceeds that size return
+ * BQL_ERR_SHAPE with nothing launched.  Nothing is allocated and nothing
+ * needs to start at zero; the first call on a device looks up that
+ * device's copy (hipGetSymbolAddress).  Every call on one GPU shares its
+ * scratch: calls that overlap in time on the same GPU (other streams, other
+ * host threads) race and must be serialized by the caller. */
+#define BQL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+bql_status bql_fp8_linear_noalloc(const void* a, bql_dtype adt, float* a_scale,
+                                  const void* w_packed, const float* w_scale, int w_per_channel,
+                                  int64_t M, int64_t N, int64_t K, const float* output_scale,
+                                  void* y, bql_dtype ydt, bql_accum accum, bql_stream stream);
+
 /* Workspace bytes for bql_w8a16_linear at this shape. */
 size_t bql_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 

@@ -103,6 +103,30 @@ def test_fp8_linear_validation(L):
     assert call(M=0, wsb=0, work=None) == OK  # no-op
 
 
+def test_fp8_linear_noalloc_validation(L):
+    # same checks as bql_fp8_linear, and shapes whose scratch exceeds the
+    # library's fixed array are refused before anything is launched
+    f = L.bql_fp8_linear_noalloc
+
+    def call(a=A16, adt=2, sa=None, w=A16, sw=A16, pc=0, M=4, N=64, K=64, os_=None, y=A16, ydt=2,
+             acc=0):
+        return f(a, adt, sa, w, sw, pc, M, N, K, os_, y, ydt, acc, None)
+
+    assert call(a=None) == ERR_NULL
+    assert call(y=MIS) == ERR_ALIGN
+    assert call(N=60) == ERR_SHAPE
+    assert call(adt=5) == ERR_DTYPE
+    assert call(acc=3) == ERR_ARG
+    assert call(adt=4) == ERR_NULL          # pre-quantized A needs a_scale
+    assert call(M=0) == OK                  # no-op
+    cap = bql.NOALLOC_SCRATCH_BYTES
+    M, N, K = 8192, 4096, 8192              # 64 MiB of packed codes + the quantizer's 8 KiB
+    assert L.bql_fp8_linear_workspace_size(M, N, K) > cap
+    assert call(M=M, N=N, K=K) == ERR_SHAPE and "noalloc" in _err(L)
+    M, N, K = 1024, 28672, 4096
+    assert L.bql_fp8_linear_workspace_size(M, N, K) <= cap
+
+
 def test_quantizer_validation(L):
     q = L.bql_fp8_quantize_dynamic
     assert q(None, 1, 10, A16, None, A16, 8192, None) == ERR_NULL
