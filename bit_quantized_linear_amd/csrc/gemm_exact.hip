@@ -1,0 +1,343 @@
+// Exact fp8 tile kernel for large M: Y = (sA*sW[n]) * sum_k dec(Aq)*dec(Wq)
+// (vLLM PR #4118, the torch._scaled_mm micro-benchmark) with every product
+// formed exactly and summed in fp32.
+//
+// The E4M3 codes are widened losslessly to fp16 in registers (every finite
+// E4M3 value is an fp16 value) and multiplied on the f16 matrix cores
+// (v_mfma_f32_16x16x32_f16), whose products are exact.  The fp8 matrix-core
+// instruction would be twice as fast but adds each run of 8 products in a
+// narrow fixed-point window, which misses the stated tolerance on outlier
+// inputs.  So the matrix-core ceiling of this kernel is the f16 one, and the
+// fp8 -> f16 conversion is vector-ALU work on top of it.
+//
+// Organisation (gfx950: 4 SIMDs per CU, 160 KiB LDS per CU):
+//   * A block computes a 256 x 256 output tile with four waves, one per SIMD,
+//     each owning a 128 x 128 sub-tile (64 accumulators of 16 x 16, 256 fp32
+//     per lane, held in the accumulation registers).  The conversions per
+//     MFMA fall with the wave tile's size: 128 x 128 needs one fp8 -> f16
+//     pair conversion per 16 MFMA cycles.
+//   * Both operands are in HBM in the 16-row x 128-k operand-tile layout
+//     (weights by prepack, activations by the quantizer).  A stage of the LDS
+//     ring is one half of a k-tile (64 k) of the block's 16 A and 16 B
+//     strips, 32 KiB, moved by LDS-DMA (buffer_load ... lds, 1 KiB per wave
+//     instruction, no VGPR staging); four stages (128 KiB) are in flight.
+//   * Per wave, a half-step is two MFMA k-slices of 8 k per lane.  Slice 0
+//     multiplies with the B operands decoded during the previous half-step,
+//     and meanwhile decodes B's slice 1 and reads the next half-step's raw B
+//     from LDS; slice 1 multiplies, decodes the next half-step's B slice 0
+//     and reads the next raw A.  Each A operand is decoded one row strip
+//     ahead of its MFMAs.  So LDS reads are consumed a whole slice (64 MFMAs)
+//     after they are issued, and the conversions run between MFMAs.
+//   * One barrier per half-step: it publishes the next stage's DMA and frees
+//     the ring slot the next DMA overwrites.
+//   * Output tiles are handed to the 8 XCDs in contiguous ranges (each XCD's
+//     L2 then holds the B strips its blocks share), and the epilogue stages
+//     each 16-row band in LDS and writes it with 16-byte stores.
+#include <atomic>
+#include <type_traits>
+
+#include "linear_common.h"
+
+namespace bql {
+
+namespace {
+
+constexpr int XB = 256;                    // block tile edge (rows and columns)
+constexpr int XW = 4;                      // waves per block (2 x 2)
+constexpr int XF = 8;                      // 16 x 16 MFMA tiles per wave edge (128 / 16)
+constexpr int XSTRIPS = XB / 16;           // 16-row strips per operand per block
+constexpr int XSTAGE = 2 * XSTRIPS * 1024; // A and B halves of one k-tile: 32 KiB
+constexpr int XS = 4;                      // LDS ring depth (stages)
+constexpr int XLDS = XS * XSTAGE;          // 128 KiB
+constexpr int XLD = 2 * XSTRIPS / XW;      // DMA instructions per wave per stage (8)
+constexpr int XEPI_ROW = XF * 16 * 4 + 16; // epilogue row: 128 fp32 values, padded
+constexpr int XEPI_WAVE = XF / 2 * 16 * XEPI_ROW;           // 64 staged rows per wave
+constexpr int XEPI_SCALES = XW * XEPI_WAVE;                 // then 128 column scales per wave
+constexpr int XLDS_EPI = XEPI_SCALES + XW * XF * 16 * 4;
+constexpr int XLDS_ALL = XLDS > XLDS_EPI ? XLDS : XLDS_EPI;
+static_assert(XLD * 2 < 64, "vmcnt range");
+
+// Eight E4M3 codes -> eight fp16 of the same values (4 conversions).
+__device__ __forceinline__ v8h dec8(uint32_t d0, uint32_t d1) { return e4m3x8_to_f16(d0, d1); }
+
+// Compiler-only fence: keeps LDS reads and writes on their side of the
+// workgroup barriers (the LDS-DMA writes are not visible to the compiler).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Scales 64 staged rows of accumulators (128 fp32 values each, XEPI_ROW
+// bytes apart) by their column's sA * sW[n] (colsc), converts them to the
+// output dtype OUT and writes them with 16-byte stores: a lane handles
+// 16 / (output size) consecutive columns per store, all of a pass's stores
+// unrolled so that their LDS reads overlap.  N is a multiple of 16, so a
+// store's columns lie all inside or all outside N.  Roundings as the other
+// kernels' epilogue: nearest even to fp16 / bf16, E4M3 of fp32(Y / output_scale).
+template <int OUT>
+__device__ __forceinline__ void store_rows_t(const LinParams& p, const float* band,
+                                             const float* colsc, int64_t rbase, int64_t col0,
+                                             int lane) {
+    constexpr int ESZ = OUT == OUT_E4M3 ? 1 : (OUT == OUT_F32 ? 4 : 2);
+    constexpr int PER = 16 / ESZ, CHUNKS = XF * 16 / PER, ITERS = XF / 2 * 16 * CHUNKS / 64;
+    const float os = OUT == OUT_E4M3 ? *p.ep.out_scale : 1.0f;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int q = lane + 64 * it;
+        const int row = q / CHUNKS, c0 = (q % CHUNKS) * PER;
+        const int64_t m = rbase + row, n = col0 + c0;
+        const float* src = band + row * (XEPI_ROW / 4) + c0;
+        float y[PER];
+#pragma unroll
+        for (int e = 0; e < PER; e += 4) {
+            const v4f x = *(const v4f*)(src + e), c = *(const v4f*)(colsc + c0 + e);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) y[e + t] = c[t] * x[t];
+        }
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            uint32_t b;
+            if constexpr (OUT == OUT_F32) b = __float_as_uint(y[e]);
+            else if constexpr (OUT == OUT_F16) b = f32_to_f16_bits(y[e]);
+            else if constexpr (OUT == OUT_BF16) b = f32_to_bf16_bits(y[e]);
+            else b = e4m3_encode(y[e] / os);
+            w[e * ESZ / 4] |= b << (8 * ((e * ESZ) % 4));
+        }
+        if (m < p.M && n < p.N)
+            *(u4*)((uint8_t*)p.ep.y + (m * p.ep.ldy + n) * ESZ) = u4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// Instruction order of one A strip's step of a slice, for the scheduler:
+// each of its 8 MFMAs is followed by one VALU instruction (the conversions
+// of the next operands; measured on gfx950, 16x16x32 MFMAs issue fastest
+// with one VALU instruction between consecutive ones, faster than back to
+// back), then the step's LDS read and, in slice 0, its DMA instruction.
+// Nothing moves across steps: a conversion pulled forward from a later step
+// could wait on an LDS read issued just before it.
+template <bool DMA>
+__device__ __forceinline__ void interleave() {
+    constexpr int MFMA = 0x008, VALU = 0x002, DS_READ = 0x100, VMEM_READ = 0x020;
+#pragma unroll
+    for (int k = 0; k < XF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VALU, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+    if constexpr (DMA) __builtin_amdgcn_sched_group_barrier(VMEM_READ, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(64 * XW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_exact_kernel(LinParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    int64_t bm, bn;
+    tile_coords(blockIdx.x, (p.M + XB - 1) / XB, (p.N + XB - 1) / XB, bm, bn);
+    const int64_t mt0 = bm * XSTRIPS, nt0 = bn * XSTRIPS;
+    const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
+    const int KT = (int)p.KT;
+
+    // Buffer descriptors over this block's strips: rows past M and channels
+    // past N lie beyond them and read as zero.
+    const int64_t a_strips = mtiles - mt0 < XSTRIPS ? mtiles - mt0 : XSTRIPS;
+    const int64_t b_strips = ntiles - nt0 < XSTRIPS ? ntiles - nt0 : XSTRIPS;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.a + mt0 * p.KT * 2048), (short)0, (int)(a_strips * p.KT * 2048),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + nt0 * p.KT * 2048), (short)0, (int)(b_strips * p.KT * 2048), 0x00020000);
+
+    // Half-step s = k-tile s/2, half s%2, goes to ring slot s % XS.  Slot q
+    // of a stage holds A strip q (q < 16) or B strip q - 16; wave w moves
+    // slots w + 4 i, i = 0..7: four A strips, then four B strips.  The first
+    // stages are issued whole (issue), the later ones one instruction per
+    // step of the main loop (issue_one), also past the last stage: those get
+    // an out-of-range offset (zeros, no memory access) into a slot nothing
+    // reads any more, so that every half-step issues the same loads.
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const int kt = s >> 1, h = s & 1;
+        uint8_t* base = lds + (s % XS) * XSTAGE;
+#pragma unroll
+        for (int i = 0; i < XLD; ++i) {
+            const int slot = wave + XW * i;
+            if (i < XLD / 2) {
+                const int off = (slot * KT + kt) * 2048 + h * 1024 + lane * 16;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + slot * 1024), 16, off,
+                                                         0, 0, 0);
+            } else {
+                const int off = ((slot - XSTRIPS) * KT + kt) * 2048 + h * 1024 + lane * 16;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + slot * 1024), 16, off,
+                                                         0, 0, 0);
+            }
+        }
+    };
+    const int H = 2 * KT;
+    const int lane16 = lane * 16;
+    auto issue_one = [&](int s, int i) __attribute__((always_inline)) {
+        const int kt = s >> 1, h = s & 1, slot = wave + XW * i;
+        uint8_t* dst = lds + (s % XS) * XSTAGE + slot * 1024;
+        // uniform part of the offset; past the last stage it lies beyond
+        // every descriptor's range (at most 2^30 bytes), so all lanes read 0
+        const int strip = i < XLD / 2 ? slot : slot - XSTRIPS;
+        const int uoff = s < H ? (strip * KT + kt) * 2048 + h * 1024 : 0x7FFF0000;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < XLD / 2 ? ra : rb, (lds_ptr_t)dst, 16, lane16 + uoff, 0,
+                                                 0, 0);
+    };
+    // A lane's 16 bytes of strip i of this wave (A) / j (B) in half-step s:
+    // bytes 0-7 feed MFMA slice 0, bytes 8-15 slice 1 (same k map for both).
+    auto read_a = [&](int s, int i) __attribute__((always_inline)) {
+        return *(const u4*)(lds + (s % XS) * XSTAGE + (wm * XF + i) * 1024 + lane * 16);
+    };
+    auto read_b = [&](int s, int j) __attribute__((always_inline)) {
+        return *(const u4*)(lds + (s % XS) * XSTAGE + (XSTRIPS + wn * XF + j) * 1024 + lane * 16);
+    };
+
+    const int64_t m0 = bm * XB + wm * XF * 16, col0 = bn * XB + wn * XF * 16;
+    // sA * sW[n] of the wave's 128 output columns (one value per tensor),
+    // kept in LDS past the operand ring until the epilogue
+    float* colsc = (float*)(lds + XEPI_SCALES) + wave * XF * 16;
+    if (lane < 16) {
+        const float sa = *p.ep.a_scale;
+#pragma unroll
+        for (int j = 0; j < XF; ++j) {
+            const int64_t n = col0 + j * 16 + lane;
+            colsc[j * 16 + lane] = sa * p.ep.w_scale[p.ep.w_per_channel ? (n < p.N ? n : p.N - 1) : 0];
+        }
+    }
+    v4f acc[XF][XF];
+#pragma unroll
+    for (int i = 0; i < XF; ++i)
+#pragma unroll
+        for (int j = 0; j < XF; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+
+#pragma unroll
+    for (int s = 0; s < XS - 1; ++s)
+        if (s < H) issue(s);
+    // stage 0 is in (stages issued after it: min(H - 1, 2)); H >= 2
+    if (H >= 3) wait_vmcnt<2 * XLD>();
+    else if (H == 2) wait_vmcnt<XLD>();
+    else wait_vmcnt<0>();
+    compiler_fence();
+    lds_barrier();
+    compiler_fence();
+
+    u4 ra_[XF], rb_[XF];   // raw codes of the current (A) / current-then-next (B) half-step
+    v8h b0[XF], b1[XF];    // decoded B slices 0 and 1
+#pragma unroll
+    for (int i = 0; i < XF; ++i) ra_[i] = read_a(0, i);
+#pragma unroll
+    for (int j = 0; j < XF; ++j) rb_[j] = read_b(0, j);
+#pragma unroll
+    for (int j = 0; j < XF; ++j) b0[j] = dec8(rb_[j][0], rb_[j][1]);
+
+    // One half-step.  The next half-step's raw operands are read from LDS
+    // during it (after the last half-step these reads see a slot nothing
+    // writes any more, and their values are never used).  Decodes are
+    // written before the MFMAs that run beside them, so that their results
+    // do not take the registers of operands those MFMAs still read.
+    auto half_step = [&](int s) __attribute__((always_inline)) {
+        // this wave's DMA of stage s+1 has landed (stage s+2 may be
+        // pending); the barrier makes every wave's share visible and tells
+        // that every wave has consumed the slot that stage s+3 overwrites
+        // (its reads completed in half-step s-1, when their data was
+        // decoded), so it needs no wait on LDS reads
+        if (s + 2 < H) wait_vmcnt<XLD>();
+        else wait_vmcnt<0>();
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+
+        // slice 0: MFMAs on b0; decode B slice 1; read the next raw B; one
+        // DMA instruction of stage s+3 per step
+        v8h a = dec8(ra_[0][0], ra_[0][1]);
+#pragma unroll
+        for (int i = 0; i < XF; ++i) {
+            v8h an;
+            if (i + 1 < XF) an = dec8(ra_[i + 1][0], ra_[i + 1][1]);
+            else an = dec8(ra_[0][2], ra_[0][3]);  // slice 1's first A operand
+            b1[i] = dec8(rb_[i][2], rb_[i][3]);
+#pragma unroll
+            for (int j = 0; j < XF; ++j) acc[i][j] = mfma_f16(a, b0[j], acc[i][j]);
+            rb_[i] = read_b(s + 1, i);
+            issue_one(s + 3, i);
+            a = an;
+            interleave<true>();
+        }
+        // slice 1: MFMAs on b1; read the next raw A; decode the next B slice 0
+#pragma unroll
+        for (int i = 0; i < XF; ++i) {
+            v8h an = a;
+            if (i + 1 < XF) an = dec8(ra_[i + 1][2], ra_[i + 1][3]);
+            ra_[i] = read_a(s + 1, i);
+            b0[i] = dec8(rb_[i][0], rb_[i][1]);
+#pragma unroll
+            for (int j = 0; j < XF; ++j) acc[i][j] = mfma_f16(a, b1[j], acc[i][j]);
+            a = an;
+            interleave<false>();
+        }
+    };
+    // the last half-step is written out after the loop: with it inside, the
+    // compiler does not keep the accumulators in place across the back edge
+    for (int s = 0; s + 1 < H; ++s) half_step(s);
+    half_step(H - 1);
+
+    // ---- epilogue, in two passes of 64 rows per wave: the fp32
+    // accumulators are staged in LDS straight from the accumulation
+    // registers (compile-time indices), then scaled by their column's
+    // sA * sW[n], converted and written with 16-byte stores
+    wait_vmcnt<0>();
+    compiler_fence();
+    __syncthreads();
+    float* band = (float*)(lds + wave * XEPI_WAVE);
+    auto stage = [&](auto ib_tag) __attribute__((always_inline)) {
+        constexpr int IB = decltype(ib_tag)::value;
+#pragma unroll
+        for (int i = 0; i < XF / 2; ++i)
+#pragma unroll
+            for (int j = 0; j < XF; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    band[(i * 16 + 4 * (lane >> 4) + r) * (XEPI_ROW / 4) + j * 16 + (lane & 15)] =
+                        acc[IB + i][j][r];
+    };
+    // the staged rows and scales are written and read back by this wave only
+    auto epilogue = [&](auto out_tag) __attribute__((always_inline)) {
+        constexpr int OUT = decltype(out_tag)::value;
+        stage(std::integral_constant<int, 0>{});
+        __builtin_amdgcn_wave_barrier();
+        store_rows_t<OUT>(p, band, colsc, m0, col0, lane);
+        __builtin_amdgcn_wave_barrier();
+        stage(std::integral_constant<int, XF / 2>{});
+        __builtin_amdgcn_wave_barrier();
+        store_rows_t<OUT>(p, band, colsc, m0 + XF / 2 * 16, col0, lane);
+    };
+    switch (p.ep.ydt) {
+        case OUT_BF16: epilogue(std::integral_constant<int, OUT_BF16>{}); break;
+        case OUT_F16: epilogue(std::integral_constant<int, OUT_F16>{}); break;
+        case OUT_F32: epilogue(std::integral_constant<int, OUT_F32>{}); break;
+        default: epilogue(std::integral_constant<int, OUT_E4M3>{}); break;
+    }
+}
+
+hipError_t launch_gemm_exact(const LinParams& p, hipStream_t stream) {
+    // dynamic LDS above 64 KiB needs the attribute, set once per device
+    // (before any graph capture: the first launch is eager)
+    static std::atomic<uint64_t> configured{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (!(configured.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute((const void*)gemm_exact_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_ALL);
+        if (e != hipSuccess) return e;
+        configured.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    const int64_t blocks = ((p.M + XB - 1) / XB) * ((p.N + XB - 1) / XB);
+    gemm_exact_kernel<<<(unsigned)blocks, 64 * XW, XLDS_ALL, stream>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace bql
