@@ -44,13 +44,13 @@ namespace {
 
 constexpr int XB = 256;                    // block tile edge (rows and columns)
 constexpr int XW = 4;                      // waves per block (2 x 2)
-constexpr int XF = 8;                      // 16 x 16 MFMA tiles per wave edge (128 / 16)
+constexpr int XF = 8;                      // 16-row A strips per wave (128 rows)
 constexpr int XSTRIPS = XB / 16;           // 16-row strips per operand per block
 constexpr int XSTAGE = 2 * XSTRIPS * 1024; // A and B halves of one k-tile: 32 KiB
 constexpr int XS = 4;                      // LDS ring depth (stages)
 constexpr int XLDS = XS * XSTAGE;          // 128 KiB
 constexpr int XLD = 2 * XSTRIPS / XW;      // DMA instructions per wave per stage (8)
-constexpr int XEPI_ROW = XF * 16 * 4 + 16; // epilogue row: 128 fp32 values, padded
+constexpr int XEPI_ROW = XF * 16 * 4 + 16; // epilogue row: up to 128 fp32 values, padded
 constexpr int XEPI_WAVE = XF / 2 * 16 * XEPI_ROW;           // 64 staged rows per wave
 constexpr int XEPI_SCALES = XW * XEPI_WAVE;                 // then 128 column scales per wave
 constexpr int XLDS_EPI = XEPI_SCALES + XW * XF * 16 * 4;
@@ -71,12 +71,13 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // unrolled so that their LDS reads overlap.  N is a multiple of 16, so a
 // store's columns lie all inside or all outside N.  Roundings as the other
 // kernels' epilogue: nearest even to fp16 / bf16, E4M3 of fp32(Y / output_scale).
-template <int OUT>
+template <int OUT, int FN>
 __device__ __forceinline__ void store_rows_t(const LinParams& p, const float* band,
                                              const float* colsc, int64_t rbase, int64_t col0,
                                              int lane) {
     constexpr int ESZ = OUT == OUT_E4M3 ? 1 : (OUT == OUT_F32 ? 4 : 2);
-    constexpr int PER = 16 / ESZ, CHUNKS = XF * 16 / PER, ITERS = XF / 2 * 16 * CHUNKS / 64;
+    constexpr int PER = 16 / ESZ, CHUNKS = FN * 16 / PER, ITERS = XF / 2 * 16 * CHUNKS / 64;
+    static_assert(XF / 2 * 16 * CHUNKS % 64 == 0, "whole stores per lane");
     const float os = OUT == OUT_E4M3 ? *p.ep.out_scale : 1.0f;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -113,14 +114,15 @@ __device__ __forceinline__ void store_rows_t(const LinParams& p, const float* ba
 // back), then the step's LDS read and, in slice 0, its DMA instruction.
 // Nothing moves across steps: a conversion pulled forward from a later step
 // could wait on an LDS read issued just before it.
-template <bool DMA>
+template <bool DMA, int FN>
 __device__ __forceinline__ void interleave() {
     constexpr int MFMA = 0x008, VALU = 0x002, DS_READ = 0x100, VMEM_READ = 0x020;
 #pragma unroll
-    for (int k = 0; k < XF; ++k) {
+    for (int k = 0; k < FN; ++k) {
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(VALU, 1, 0);
     }
+    if constexpr (FN < XF) __builtin_amdgcn_sched_group_barrier(VALU, XF - FN, 0);
     __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
     if constexpr (DMA) __builtin_amdgcn_sched_group_barrier(VMEM_READ, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -128,21 +130,26 @@ __device__ __forceinline__ void interleave() {
 
 }  // namespace
 
+// FN: 16-column B strips per wave (8: 256 x 256 blocks; 7: 256 x 224, whose
+// stages still carry 16 B slots, the last two loaded out of range as zeros
+// and never read, so that every wave moves the same 8 KiB per stage).
+template <int FN>
 __global__ __launch_bounds__(64 * XW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_exact_kernel(LinParams p) {
+    constexpr int BN = 32 * FN;  // block columns
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     int64_t bm, bn;
-    tile_coords(blockIdx.x, (p.M + XB - 1) / XB, (p.N + XB - 1) / XB, bm, bn);
-    const int64_t mt0 = bm * XSTRIPS, nt0 = bn * XSTRIPS;
+    tile_coords(blockIdx.x, (p.M + XB - 1) / XB, (p.N + BN - 1) / BN, bm, bn);
+    const int64_t mt0 = bm * XSTRIPS, nt0 = bn * (2 * FN);
     const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
     const int KT = (int)p.KT;
 
     // Buffer descriptors over this block's strips: rows past M and channels
     // past N lie beyond them and read as zero.
     const int64_t a_strips = mtiles - mt0 < XSTRIPS ? mtiles - mt0 : XSTRIPS;
-    const int64_t b_strips = ntiles - nt0 < XSTRIPS ? ntiles - nt0 : XSTRIPS;
+    const int64_t b_strips = ntiles - nt0 < 2 * FN ? ntiles - nt0 : 2 * FN;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)p.a + mt0 * p.KT * 2048), (short)0, (int)(a_strips * p.KT * 2048),
         0x00020000);
@@ -191,26 +198,26 @@ void gemm_exact_kernel(LinParams p) {
         return *(const u4*)(lds + (s % XS) * XSTAGE + (wm * XF + i) * 1024 + lane * 16);
     };
     auto read_b = [&](int s, int j) __attribute__((always_inline)) {
-        return *(const u4*)(lds + (s % XS) * XSTAGE + (XSTRIPS + wn * XF + j) * 1024 + lane * 16);
+        return *(const u4*)(lds + (s % XS) * XSTAGE + (XSTRIPS + wn * FN + j) * 1024 + lane * 16);
     };
 
-    const int64_t m0 = bm * XB + wm * XF * 16, col0 = bn * XB + wn * XF * 16;
+    const int64_t m0 = bm * XB + wm * XF * 16, col0 = bn * BN + wn * FN * 16;
     // sA * sW[n] of the wave's 128 output columns (one value per tensor),
     // kept in LDS past the operand ring until the epilogue
     float* colsc = (float*)(lds + XEPI_SCALES) + wave * XF * 16;
     if (lane < 16) {
         const float sa = *p.ep.a_scale;
 #pragma unroll
-        for (int j = 0; j < XF; ++j) {
+        for (int j = 0; j < FN; ++j) {
             const int64_t n = col0 + j * 16 + lane;
             colsc[j * 16 + lane] = sa * p.ep.w_scale[p.ep.w_per_channel ? (n < p.N ? n : p.N - 1) : 0];
         }
     }
-    v4f acc[XF][XF];
+    v4f acc[XF][FN];
 #pragma unroll
     for (int i = 0; i < XF; ++i)
 #pragma unroll
-        for (int j = 0; j < XF; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0, 0, 0, 0};
 
 #pragma unroll
     for (int s = 0; s < XS - 1; ++s)
@@ -223,14 +230,14 @@ void gemm_exact_kernel(LinParams p) {
     lds_barrier();
     compiler_fence();
 
-    u4 ra_[XF], rb_[XF];   // raw codes of the current (A) / current-then-next (B) half-step
-    v8h b0[XF], b1[XF];    // decoded B slices 0 and 1
+    u4 ra_[XF], rb_[FN];   // raw codes of the current (A) / current-then-next (B) half-step
+    v8h b0[FN], b1[FN];    // decoded B slices 0 and 1
 #pragma unroll
     for (int i = 0; i < XF; ++i) ra_[i] = read_a(0, i);
 #pragma unroll
-    for (int j = 0; j < XF; ++j) rb_[j] = read_b(0, j);
+    for (int j = 0; j < FN; ++j) rb_[j] = read_b(0, j);
 #pragma unroll
-    for (int j = 0; j < XF; ++j) b0[j] = dec8(rb_[j][0], rb_[j][1]);
+    for (int j = 0; j < FN; ++j) b0[j] = dec8(rb_[j][0], rb_[j][1]);
 
     // One half-step.  The next half-step's raw operands are read from LDS
     // during it (after the last half-step these reads see a slot nothing
@@ -257,13 +264,13 @@ void gemm_exact_kernel(LinParams p) {
             v8h an;
             if (i + 1 < XF) an = dec8(ra_[i + 1][0], ra_[i + 1][1]);
             else an = dec8(ra_[0][2], ra_[0][3]);  // slice 1's first A operand
-            b1[i] = dec8(rb_[i][2], rb_[i][3]);
+            if (i < FN) b1[i] = dec8(rb_[i][2], rb_[i][3]);
 #pragma unroll
-            for (int j = 0; j < XF; ++j) acc[i][j] = mfma_f16(a, b0[j], acc[i][j]);
-            rb_[i] = read_b(s + 1, i);
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma_f16(a, b0[j], acc[i][j]);
+            if (i < FN) rb_[i] = read_b(s + 1, i);
             issue_one(s + 3, i);
             a = an;
-            interleave<true>();
+            interleave<true, FN>();
         }
         // slice 1: MFMAs on b1; read the next raw A; decode the next B slice 0
 #pragma unroll
@@ -271,11 +278,11 @@ void gemm_exact_kernel(LinParams p) {
             v8h an = a;
             if (i + 1 < XF) an = dec8(ra_[i + 1][2], ra_[i + 1][3]);
             ra_[i] = read_a(s + 1, i);
-            b0[i] = dec8(rb_[i][0], rb_[i][1]);
+            if (i < FN) b0[i] = dec8(rb_[i][0], rb_[i][1]);
 #pragma unroll
-            for (int j = 0; j < XF; ++j) acc[i][j] = mfma_f16(a, b1[j], acc[i][j]);
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma_f16(a, b1[j], acc[i][j]);
             a = an;
-            interleave<false>();
+            interleave<false, FN>();
         }
     };
     // the last half-step is written out after the loop: with it inside, the
@@ -296,7 +303,7 @@ void gemm_exact_kernel(LinParams p) {
 #pragma unroll
         for (int i = 0; i < XF / 2; ++i)
 #pragma unroll
-            for (int j = 0; j < XF; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     band[(i * 16 + 4 * (lane >> 4) + r) * (XEPI_ROW / 4) + j * 16 + (lane & 15)] =
@@ -307,11 +314,11 @@ void gemm_exact_kernel(LinParams p) {
         constexpr int OUT = decltype(out_tag)::value;
         stage(std::integral_constant<int, 0>{});
         __builtin_amdgcn_wave_barrier();
-        store_rows_t<OUT>(p, band, colsc, m0, col0, lane);
+        store_rows_t<OUT, FN>(p, band, colsc, m0, col0, lane);
         __builtin_amdgcn_wave_barrier();
         stage(std::integral_constant<int, XF / 2>{});
         __builtin_amdgcn_wave_barrier();
-        store_rows_t<OUT>(p, band, colsc, m0 + XF / 2 * 16, col0, lane);
+        store_rows_t<OUT, FN>(p, band, colsc, m0 + XF / 2 * 16, col0, lane);
     };
     switch (p.ep.ydt) {
         case OUT_BF16: epilogue(std::integral_constant<int, OUT_BF16>{}); break;
@@ -321,7 +328,8 @@ void gemm_exact_kernel(LinParams p) {
     }
 }
 
-hipError_t launch_gemm_exact(const LinParams& p, hipStream_t stream) {
+template <int FN>
+static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
     // dynamic LDS above 64 KiB needs the attribute, set once per device
     // (before any graph capture: the first launch is eager)
     static std::atomic<uint64_t> configured{0};
@@ -330,14 +338,26 @@ hipError_t launch_gemm_exact(const LinParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const uint64_t bit = uint64_t(1) << (dev & 63);
     if (!(configured.load(std::memory_order_acquire) & bit)) {
-        e = hipFuncSetAttribute((const void*)gemm_exact_kernel,
+        e = hipFuncSetAttribute((const void*)gemm_exact_kernel<FN>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_ALL);
         if (e != hipSuccess) return e;
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
-    const int64_t blocks = ((p.M + XB - 1) / XB) * ((p.N + XB - 1) / XB);
-    gemm_exact_kernel<<<(unsigned)blocks, 64 * XW, XLDS_ALL, stream>>>(p);
+    const int64_t blocks = ((p.M + XB - 1) / XB) * ((p.N + 32 * FN - 1) / (32 * FN));
+    gemm_exact_kernel<FN><<<(unsigned)blocks, 64 * XW, XLDS_ALL, stream>>>(p);
     return hipGetLastError();
+}
+
+// One block per CU at a time: the busiest CU runs ceil(tiles / CUs) tiles,
+// so 224-column tiles win where they even the rounds out (M = 1024,
+// N = 28672: 448 tiles of 256 take two rounds, 512 of 224 two rounds of
+// 7/8 the work).
+hipError_t launch_gemm_exact(const LinParams& p, hipStream_t stream) {
+    constexpr int64_t CUS = 256;
+    const int64_t mt = (p.M + XB - 1) / XB;
+    const int64_t t8 = mt * ((p.N + 255) / 256), t7 = mt * ((p.N + 223) / 224);
+    if (((t7 + CUS - 1) / CUS) * 224 < ((t8 + CUS - 1) / CUS) * 256) return launch_fn<7>(p, stream);
+    return launch_fn<8>(p, stream);
 }
 
 }  // namespace bql
