@@ -78,6 +78,7 @@ def _declare(L):
     L.bqo_w4a8_acc.argtypes = [_P, _P, _I64, _I64, _I64, _P, _I64, _P]
     L.bqo_w4a8_linear.argtypes = [_P, _P, _P, _I64, _P, _I64, _P]
     L.bqo_w4a8_group_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P]
+    L.bqo_w4a16_group_linear.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P]
     L.bqo_rms_sumsq.restype = ctypes.c_double
     L.bqo_rms_sumsq.argtypes = [_P, _I64]
     L.bqo_rms_inv.restype = ctypes.c_float
@@ -88,7 +89,7 @@ def _declare(L):
                "bqo_quant_with_scales", "bqo_int8_quant_per_token", "bqo_unpack_int4",
                "bqo_fp8_acc", "bqo_fp8_linear", "bqo_fp8_output", "bqo_w8a16_linear",
                "bqo_w4a8_acc", "bqo_w4a8_linear", "bqo_rmsnorm_apply", "bqo_rmsnorm",
-               "bqo_w4a8_group_linear"):
+               "bqo_w4a8_group_linear", "bqo_w4a16_group_linear"):
         getattr(L, fn).restype = None
 
 
@@ -362,6 +363,24 @@ def w4a8_group_linear(aq, sa, w4, sw, group=128, rows=None) -> np.ndarray:
     y = np.empty((r.size, N), dtype=np.float64)
     lib().bqo_w4a8_group_linear(_ptr(aq), _ptr(sa), _ptr(w4), _ptr(sw), M, N, K, group, _ptr(r),
                                 r.size, _ptr(y))
+    return y
+
+
+def w4a16_group_linear(a, w4, sw, group=128, rows=None) -> np.ndarray:
+    """Per-group weight-only int4 (QQQ issue #15 "awq-g128" / "marlin-g128",
+    read as one scale per output channel and 128-k group, no zero point):
+    Y = sum_g sW[n,g] * sum_{k in g} A[m,k] * W4[n,k], fp64.  a: fp32 values
+    of the fp16 activations [M, K]; w4: int values [N, K]; sw: [N, G]."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    w4 = np.ascontiguousarray(w4, dtype=np.int8)
+    M, K = a.shape
+    N = w4.shape[0]
+    G = (K + group - 1) // group
+    sw = np.ascontiguousarray(sw, dtype=np.float32).reshape(N, G)
+    r = _rows(rows, M)
+    y = np.empty((r.size, N), dtype=np.float64)
+    lib().bqo_w4a16_group_linear(_ptr(a), _ptr(w4), _ptr(sw), M, N, K, group, _ptr(r), r.size,
+                                 _ptr(y))
     return y
 
 

@@ -31,6 +31,9 @@
  *  - Per-group W4A8, one scale per output channel and 128-k group (QQQ
  *    issue #15, the "qqq-g128" columns), with the reading stated at
  *    bqo_w4a8_group_linear below.
+ *  - Per-group weight-only int4 (W4A16) with fp16 activations (QQQ issue
+ *    #15, the "awq-g128" and "marlin-g128" columns), with the reading
+ *    stated at bqo_w4a16_group_linear below.
  *
  * Readings where the pages are silent are ours and are listed in the design
  * notes: RNE, saturation to +-448, sign kept on zero/underflow, IEEE fp32
@@ -386,6 +389,38 @@ void bqo_w4a8_group_linear(const int8_t* aq, const float* sa, const int8_t* w4, 
                 sum += (double)sw[n * G + g] * (double)acc;
             }
             y[r * N + n] = (double)sa[m] * sum;
+        }
+    }
+    (void)M;
+}
+
+/* ------------------------------------------------ per-group W4A16 (g128) */
+
+/* The QQQ issue #15 tables also list weight-only int4 kernels with group
+ * size 128 ("awq-g128", "marlin-g128"): 16-bit activations, int4 weights,
+ * one scale per output channel and group; the pages give no formula.  The
+ * plain reading used here, the same weight format as the per-group W4A8
+ * above (two's-complement int4, no zero point):
+ *   Y[m,n] = sum_g sW[n,g] * sum_{k in group g} A[m,k] * W4[n,k]
+ * with A the fp32 values of the fp16 activations; computed in fp64 for the
+ * given rows (sW: [N][G] row-major). */
+void bqo_w4a16_group_linear(const float* a, const int8_t* w4, const float* sw, int64_t M,
+                            int64_t N, int64_t K, int64_t group, const int64_t* rows,
+                            int64_t nrows, double* y) {
+    const int64_t G = (K + group - 1) / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t m = rows[r];
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double part = 0.0;
+                const int64_t k1 = (g + 1) * group < K ? (g + 1) * group : K;
+                for (int64_t k = g * group; k < k1; ++k)
+                    part += (double)a[m * K + k] * (double)w4[n * K + k];
+                sum += (double)sw[n * G + g] * part;
+            }
+            y[r * N + n] = sum;
         }
     }
     (void)M;
