@@ -430,15 +430,18 @@ def bench_w4a8(bql, dev, steps, warmup):
     return out
 
 
-def bench_w4a8_group(bql, dev, steps, warmup):
-    """Per-group W4A8 (one scale per channel and 128-k group) over the W4A8
-    shapes K = N in {4096, 5120, 6656, 8192}: M = 1024 in TOP/s and M = 1 in
-    GB/s of algorithmic bytes (N*K/2 + N*K/128*4 group scales + M*K + 4M +
-    2MN)."""
+def bench_int4_group(bql, dev, steps, warmup, fp16_act=False):
+    """Per-group int4 weights (one fp16 scale per channel and 128-k group)
+    over the W4A8 shapes K = N in {4096, 5120, 6656, 8192}, with int8
+    per-token activations (W4A8) or fp16 activations (weight-only W4A16):
+    M = 1024 in TOP/s (TFLOP/s for fp16) and M = 1 in GB/s of algorithmic
+    bytes (N*K/2 + N*K/128*4 group scales + the activations, their scales
+    and the fp16 output)."""
     shapes = wl.CFG5_KN
+    seed = 94 if fp16_act else 95
     rots = []
     for idx, n in enumerate(shapes):
-        g = wl.rng(95, idx, 1)
+        g = wl.rng(seed, idx, 1)
         w4 = wl.int4_weight(g, n, n)
         s = (g.uniform(0.5, 2.0, size=(n, n // 128)) * 2.0 ** -8).astype(np.float16)
         wpk = torch.from_numpy(wl.pack_int4(w4).reshape(n, n // 2)).to(dev)
@@ -446,27 +449,31 @@ def bench_w4a8_group(bql, dev, steps, warmup):
         pw = bql.prepack_weight(wpk, "int4_group", scales=sc)
         rots.append(rotation(pw, bql, n * n // 2))
     nslots = max(len(r) for r in rots)
-    out = {"workload": "per-group W4A8 linears (g128) K=N in {4096,5120,6656,8192}: int4 weights "
-                       "U{-8..7} with fp16 scales U[0.5,2]*2^-8 per channel and 128-k group, int8 "
-                       "per-token activations from fp16 N(0,1), fp16 out"}
+    act = "fp16 N(0,1) activations" if fp16_act else "int8 per-token activations from fp16 N(0,1)"
+    out = {"workload": f"per-group {'W4A16' if fp16_act else 'W4A8'} linears (g128) K=N in "
+                       "{4096,5120,6656,8192}: int4 weights U{-8..7} with fp16 scales U[0.5,2]*2^-8 "
+                       f"per channel and 128-k group, {act}, fp16 out"}
     for M in (1024, 1):
-        aqs, sas, ys, wss = [], [], [], []
+        acts, ys, wss = [], [], []
         for idx, n in enumerate(shapes):
-            a = torch.from_numpy(wl.activation(wl.rng(95, idx, M, 3), M, n, "f16").view(np.int16)).to(dev)
-            aq, sa = bql.int8_quantize_per_token(a.view(torch.float16))
-            aqs.append(aq)
-            sas.append(sa)
+            a = torch.from_numpy(wl.activation(wl.rng(seed, idx, M, 3), M, n, "f16").view(np.int16)).to(dev)
+            acts.append(a.view(torch.float16) if fp16_act else bql.int8_quantize_per_token(a.view(torch.float16)))
             ys.append(torch.empty((M, n), dtype=torch.float16, device=dev))
-            wss.append(torch.empty(max(256, bql.lib().bql_w4a8_linear_workspace_size(M, n, n)),
-                                   dtype=torch.uint8, device=dev))
+            wsb = (bql.lib().bql_w4a16_linear_workspace_size(M, n, n) if fp16_act
+                   else bql.lib().bql_w4a8_linear_workspace_size(M, n, n))
+            wss.append(torch.empty(max(256, wsb), dtype=torch.uint8, device=dev))
 
         def step(i):
             for j in range(len(shapes)):
                 r = rots[j]
-                bql.w4a8_group_linear(aqs[j], sas[j], r[i % len(r)], out=ys[j], ws=wss[j])
+                if fp16_act:
+                    bql.w4a16_group_linear(acts[j], r[i % len(r)], out=ys[j], ws=wss[j])
+                else:
+                    bql.w4a8_group_linear(acts[j][0], acts[j][1], r[i % len(r)], out=ys[j], ws=wss[j])
         sec = timed_graphs(step, nslots, steps, warmup, per_graph=1 if M > 16 else SMALL_STEPS_PER_GRAPH)
         ops = sum(2 * M * n * n for n in shapes)
-        byts = sum(n * n // 2 + n * (n // 128) * 4 + M * n + 4 * M + 2 * M * n for n in shapes)
+        abytes = (lambda n: 2 * M * n) if fp16_act else (lambda n: M * n + 4 * M)
+        byts = sum(n * n // 2 + n * (n // 128) * 4 + abytes(n) + 2 * M * n for n in shapes)
         if M == 1:
             gbs = byts / sec / 1e9
             out["M1"] = {"value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(sec * 1e6, 2),
@@ -474,9 +481,11 @@ def bench_w4a8_group(bql, dev, steps, warmup):
                                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
         else:
             tops = ops / sec / 1e12
-            out[f"M{M}"] = {"value": round(tops, 1), "unit": "TOP/s", "us_per_step": round(sec * 1e6, 2),
-                            "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_I8_TOPS,
-                                         "unit": "TOP/s", "frac": round(tops / PEAK_I8_TOPS, 4)}}
+            peak = PEAK_F16_TFLOPS if fp16_act else PEAK_I8_TOPS
+            unit = "TFLOP/s" if fp16_act else "TOP/s"
+            out[f"M{M}"] = {"value": round(tops, 1), "unit": unit, "us_per_step": round(sec * 1e6, 2),
+                            "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": peak,
+                                         "unit": unit, "frac": round(tops / peak, 4)}}
     return out
 
 
@@ -792,7 +801,7 @@ def main():
     ap.add_argument("--rmsnorm-only", action="store_true",
                     help="only the fused RMSNorm + quantization leg (for a rocprofv3 run of it)")
     ap.add_argument("--w4a8-group-only", action="store_true",
-                    help="only the per-group W4A8 leg (for a rocprofv3 run of it)")
+                    help="only the per-group W4A8 and W4A16 legs (for a rocprofv3 run of them)")
     ap.add_argument("--small-n-only", action="store_true",
                     help="only the small-N (MoE router) leg (for a rocprofv3 run of it)")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
@@ -820,7 +829,8 @@ def main():
               flush=True)
         return
     if args.w4a8_group_only:
-        print(json.dumps({"w4a8_group": bench_w4a8_group(bql, dev, args.steps, args.warmup)}),
+        print(json.dumps({"w4a8_group": bench_int4_group(bql, dev, args.steps, args.warmup),
+                          "w4a16_group": bench_int4_group(bql, dev, args.steps, args.warmup, True)}),
               flush=True)
         return
     if args.small_n_only:
@@ -939,7 +949,9 @@ def main():
     log("timing small N ...")
     small_n = bench_small_n(bql, dev, args.steps, args.warmup)
     log("timing W4A8 per group ...")
-    w4a8_group = bench_w4a8_group(bql, dev, args.steps, args.warmup)
+    w4a8_group = bench_int4_group(bql, dev, args.steps, args.warmup)
+    log("timing W4A16 per group ...")
+    w4a16_group = bench_int4_group(bql, dev, args.steps, args.warmup, fp16_act=True)
 
     out = {
         "metric": METRIC,
@@ -991,6 +1003,7 @@ def main():
         "rmsnorm_quant": norm_quant,
         "small_n": small_n,
         "w4a8_group": w4a8_group,
+        "w4a16_group": w4a16_group,
     }
     if not args.no_config_rows:
         out["configs"] = bench_configs(bql, dev, args.steps, args.warmup, args.oracle_sample_rows)

@@ -21,6 +21,7 @@ Operations (see the header for the exact contracts):
   w8a16_linear            Y = sW[n] (A Wq^T), fp16 activations
   w4a8_linear             int4 x int8 with int32 accumulation
   w4a8_group_linear       the same with a scale per channel and 128-k group
+  w4a16_group_linear      fp16 x int4 weight-only, a scale per channel and 128-k group
 """
 from __future__ import annotations
 
@@ -83,6 +84,8 @@ SIGNATURES = {
     "bql_w4a8_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "bql_w4a8_linear": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "bql_w4a8_group_linear": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "bql_w4a16_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "bql_w4a16_group_linear": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -386,6 +389,28 @@ def w4a8_group_linear(aq: torch.Tensor, a_scales: torch.Tensor, pw: PackedWeight
            L.bql_w4a8_group_linear(_ptr(aq), _ptr(a_scales), _ptr(pw.packed), _ptr(pw.scales), M, N,
                                    K, 128, _ptr(out), _TORCH_TO_BQL[out_dtype], _ptr(ws), nb,
                                    _stream(aq.device)))
+    return out
+
+
+def w4a16_group_linear(a: torch.Tensor, pw: PackedWeight, out_dtype: torch.dtype = torch.float16,
+                       out: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp16 [M,K] activations x int4 weight with a scale per output channel
+    and 128-k group (prepacked as "int4_group"), weight-only."""
+    _need_cuda(a, out, ws)
+    L = lib()
+    M, K = a.shape
+    N = pw.N
+    if pw.fmt != "int4_group":
+        raise ValueError("w4a16_group_linear takes an int4_group weight")
+    if a.dtype != torch.float16:
+        raise ValueError("w4a16_group_linear takes fp16 activations")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    ws, nb = _workspace(L.bql_w4a16_linear_workspace_size(M, N, K), a.device, ws)
+    _check("bql_w4a16_group_linear",
+           L.bql_w4a16_group_linear(_ptr(a), _ptr(pw.packed), _ptr(pw.scales), M, N, K, 128, _ptr(out),
+                                    _TORCH_TO_BQL[out_dtype], _ptr(ws), nb, _stream(a.device)))
     return out
 
 

@@ -651,4 +651,43 @@ bql_status bql_w4a8_group_linear(const int8_t* aq, const float* a_scales, const 
                                          (hipStream_t)stream));
 }
 
+size_t bql_w4a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return align256(bql::small_m_ws_bytes(M, N, K, bql::V_W4A16G));
+}
+
+bql_status bql_w4a16_group_linear(const void* a, const void* w_packed, const float* w_scales,
+                                  int64_t M, int64_t N, int64_t K, int64_t group_size, void* y,
+                                  bql_dtype ydt, void* ws, size_t ws_bytes, bql_stream stream) {
+    CHECK(need_m(M));
+    CHECK(need_nk(N, K));
+    if (M > (int64_t(65535) * 16)) return fail(BQL_ERR_SHAPE, "M above 1048560");
+    if (group_size != 128) return fail(BQL_ERR_ARG, "group_size must be 128");
+    if (K % 128) return fail(BQL_ERR_SHAPE, "K=%lld must be a multiple of 128", (long long)K);
+    if (N * (K / 128) * 4 >= (int64_t(1) << 31))
+        return fail(BQL_ERR_SHAPE, "N * K/128 group scales must fit in 2 GiB");
+    if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32)
+        return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16 or BQL_F32");
+    if (M == 0) return ok();
+    CHECK(need_ptr(a, "a"));
+    CHECK(need_ptr(w_packed, "w_packed"));
+    CHECK(need_ptr(w_scales, "w_scales"));
+    CHECK(need_ptr(y, "y"));
+    CHECK(need_ws(ws, ws_bytes, bql_w4a16_linear_workspace_size(M, N, K)));
+    bql::LinearArgs la;
+    la.variant = bql::V_W4A16G;
+    la.a = a;
+    la.w = (const uint8_t*)w_packed;
+    la.M = M;
+    la.N = N;
+    la.K = K;
+    la.y = y;
+    la.ydt = ydt;
+    la.a_scale = nullptr;
+    la.w_scale = w_scales;
+    la.w_per_channel = 1;
+    la.out_scale = nullptr;
+    return hip_status(bql::launch_linear(la, ws, ws_bytes, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -226,6 +226,35 @@ __device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t d0, uint32_t d1) {
     return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
+// Four int4 values (the low nibbles of a dword's bytes, k in byte order) ->
+// four fp16 of the same values, two per dword.  Each nibble n (two's
+// complement) becomes n ^ 8 in 0..15; a byte permute places it under the
+// exponent byte 0x64, which is the fp16 value 1024 + (n ^ 8), and one packed
+// fp16 subtraction of 1032 leaves n exactly.
+__device__ __forceinline__ void int4x4_to_f16(uint32_t nibbles, uint32_t& lo, uint32_t& hi) {
+    const uint32_t x = (nibbles & 0x0F0F0F0Fu) ^ 0x08080808u;
+    // v_perm_b32 selectors: 0-3 pick bytes of x, 4 a byte of 0x64646464
+    const v2h l = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+    const v2h h = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+    lo = __builtin_bit_cast(uint32_t, l - v2h{(_Float16)1032.0f, (_Float16)1032.0f});
+    hi = __builtin_bit_cast(uint32_t, h - v2h{(_Float16)1032.0f, (_Float16)1032.0f});
+}
+
+// A lane's 16 packed int4 bytes (32 values: byte j holds k = k0 + j in its
+// low nibble and k0 + 16 + j in its high nibble) -> four fp16 operands of
+// 8 consecutive k: k0 .. k0+7, k0+8 .., k0+16 .., k0+24 ...
+__device__ __forceinline__ void int4x32_to_f16(const uint32_t (&d)[4], v8h (&h)[4]) {
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int4x4_to_f16(d[i], w[2 * i], w[2 * i + 1]);            // low nibbles: k0 + 4i ..
+        int4x4_to_f16(d[i] >> 4, w[8 + 2 * i], w[8 + 2 * i + 1]);  // high nibbles: k0 + 16 + 4i ..
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        h[q] = __builtin_bit_cast(v8h, v4i{(int)w[4 * q], (int)w[4 * q + 1], (int)w[4 * q + 2], (int)w[4 * q + 3]});
+}
+
 // Sixteen int4 values (one dword pair of a lane's packed bytes) -> int8
 // operands multiplied by 16: low nibbles shifted up, high nibbles masked.
 __device__ __forceinline__ uint32_t int4_lo_x16(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }

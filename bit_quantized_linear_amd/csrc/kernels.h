@@ -73,9 +73,11 @@ hipError_t launch_unpack_int4(const uint8_t* packed, int64_t N, int64_t K, uint8
 //        accumulation); V_FP8X: E4M3 x E4M3 decoded losslessly to fp16 and
 //        summed exactly on the f16 matrix cores; V_W8A16: fp16 x E4M3 on the
 //        f16 matrix cores; V_W4A8: int8 x int4 on the int8 matrix cores.
+//        V_W4A16G: fp16 x int4 (weight-only) with one scale per output
+//        channel and 128-k group, each group summed on the f16 matrix cores;
 //        V_W4A8G: V_W4A8 with one scale per output channel and 128-k group,
 //        applied to each k-tile's exact int32 sum, summed in fp32.
-enum Variant { V_FP8 = 0, V_W8A16 = 1, V_W4A8 = 2, V_FP8X = 3, V_W4A8G = 4 };
+enum Variant { V_FP8 = 0, V_W8A16 = 1, V_W4A8 = 2, V_FP8X = 3, V_W4A8G = 4, V_W4A16G = 5 };
 // Longest K of the per-group path, in 128-k tiles (its block stages the
 // group scales of all k-tiles in LDS).
 constexpr int W4A8G_MAX_KT = 128;
@@ -89,7 +91,7 @@ struct LinearArgs {
     void* y;
     int ydt;
     const float* a_scale;   // fp8: device scalar; w4a8: [M]
-    const float* w_scale;   // V_W4A8G: group scales [K/128][N]
+    const float* w_scale;   // V_W4A8G, V_W4A16G: group scales [K/128][N]
     int w_per_channel;
     const float* out_scale;
     // fused small-M fp8: A is row-major fp16/bf16 and is quantized in-kernel

@@ -47,7 +47,7 @@ namespace bql {
 template <int V>
 struct ALoader {
     static constexpr int CH = VT<V>::A_CHUNKS;
-    static constexpr int KC = V == V_W8A16 ? 8 : 16;  // k per 16-byte chunk
+    static constexpr int KC = (V == V_W8A16 || V == V_W4A16G) ? 8 : 16;  // k per 16-byte chunk
     __amdgpu_buffer_rsrc_t rs;
     uint32_t base, skt, sc;  // lane's byte offset at kt = 0; strides per k-tile and per chunk
     int64_t kcol, klim;      // k of the lane's first element at kt = 0; chunks at k >= klim read zero
@@ -59,7 +59,7 @@ struct ALoader {
         klim = kt_end * TILE_K < p.K ? kt_end * TILE_K : p.K;
         const uint8_t* ptr;
         int64_t bytes;
-        if (V == V_W8A16) {
+        if (V == V_W8A16 || V == V_W4A16G) {
             ptr = (const uint8_t*)p.a + mt * 16 * p.K * 2;
             bytes = rows * p.K * 2;
             base = (uint32_t)((r * p.K + kcol) * 2);
@@ -102,7 +102,7 @@ struct ALoader {
 // register room for two weight batches, A and the decoded operands without
 // spilling, and as many resident blocks as that leaves.
 constexpr int gemv_min_waves(int v, bool fused) {
-    return (fused || v == V_FP8 || v == V_W4A8) ? 6 : 5;  // V_W4A8G: 5
+    return (fused || v == V_FP8 || v == V_W4A8) ? 6 : 5;  // V_W8A16, V_W4A8G, V_W4A16G: 5
 }
 
 template <int V, int NT, int WAVES, int U, bool FUSED>
@@ -127,9 +127,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
     const int64_t strips = ntiles - nt0 < NT ? ntiles - nt0 : NT;
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.w + nt0 * p.KT * BT), (short)0, (int)(strips * p.KT * BT), 0x00020000);
-    // V_W4A8G: group scales [KT][N] fp32
+    // V_W4A8G, V_W4A16G: group scales [KT][N] fp32
     [[maybe_unused]] const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.ep.w_scale, (short)0, (int)(V == V_W4A8G ? p.KT * p.N * 4 : 0), 0x00020000);
+        (void*)p.ep.w_scale, (short)0, (int)((V == V_W4A8G || V == V_W4A16G) ? p.KT * p.N * 4 : 0),
+        0x00020000);
     // Weight tiles for k-tiles kt, kt + WAVES, ... (U of them) of this wave;
     // tiles past this split's k range (or past N) read as zero.
     auto load_batch = [&](int64_t kt, u4 (&b)[U][NT][VT<V>::B_CHUNKS]) {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
             for (int j = 0; j < NT; ++j) {
                 const bool ok = k < kt_end && j < strips;
                 const uint32_t off = (uint32_t)((j * p.KT + k) * BT) + lane * 16;
-                if constexpr (V == V_W4A8G) {
+                if constexpr (V == V_W4A8G || V == V_W4A16G) {
                     // the weight tile, then this k-tile's scale of the lane's channel
                     b[u][j][0] = __builtin_bit_cast(
                         u4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(ok ? off : OOB), 0, 2));
@@ -988,7 +989,7 @@ constexpr int64_t FUSED_LDS = 48 * 1024;   // bytes of A codes a fused block may
 
 bool use_small_m(int variant, int64_t M, int64_t N, int64_t K) {
     (void)N; (void)K;
-    return variant == V_W8A16 || M <= SMALL_M;
+    return variant == V_W8A16 || variant == V_W4A16G || M <= SMALL_M;
 }
 
 struct GemvPlan {
@@ -1200,6 +1201,7 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
             case V_FP8X: return run_gemv<V_FP8X, false>(p, stream);
             case V_W8A16: return run_gemv<V_W8A16, false>(p, stream);
             case V_W4A8G: return run_gemv<V_W4A8G, false>(p, stream);
+            case V_W4A16G: return run_gemv<V_W4A16G, false>(p, stream);
             default: return run_gemv<V_W4A8, false>(p, stream);
         }
     }

@@ -58,6 +58,15 @@ template <> struct VT<V_W4A8> {
 };
 // Per-group W4A8: the B operand of the small-M kernels carries the k-tile's
 // group scale of the lane's channel as a second chunk (x component).
+// Per-group W4A16: fp16 A as W8A16, the int4 tile and the k-tile's group
+// scale as V_W4A8G.
+template <> struct VT<V_W4A16G> {
+    static constexpr int B_TILE = INT4_TILE_BYTES;
+    static constexpr int A_CHUNKS = 4;
+    static constexpr int B_CHUNKS = 2;
+    using Acc = v4f;
+    using E = float;
+};
 template <> struct VT<V_W4A8G> {
     static constexpr int B_TILE = INT4_TILE_BYTES;
     static constexpr int A_CHUNKS = 2;
@@ -115,6 +124,18 @@ __device__ __forceinline__ void mma(typename VT<V>::Acc& acc, const u4 (&a)[VT<V
         mma_w4a8(acc, a[0], a[1], b[0]);
     } else if constexpr (V == V_W4A8G) {
         group_fold(acc, a[0], a[1], b[0], __uint_as_float(b[1][0]) * 0.0625f);
+    } else if constexpr (V == V_W4A16G) {
+        // the k-tile is one 128-k group: its sum over the f16 matrix cores
+        // (exact products), then times the group scale into fp32
+        const uint32_t d[4] = {b[0][0], b[0][1], b[0][2], b[0][3]};
+        v8h bh[4];
+        int4x32_to_f16(d, bh);
+        v4f t = v4f{0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t = mfma_f16(__builtin_bit_cast(v8h, a[q]), bh[q], t);
+        const float s = __uint_as_float(b[1][0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(t[r], s, acc[r]);
     } else if constexpr (V == V_FP8X) {
         // four f16 MFMAs over k0+8q .. k0+8q+7 on losslessly decoded codes
         v8h ah[4], bh[4];
@@ -135,6 +156,7 @@ __device__ __forceinline__ void finish(const LinParams& p, float sa, int64_t m, 
                                        typename VT<V>::E v) {
     if constexpr (V == V_W4A8) epilogue_int(p.ep, m, n, v);
     else if constexpr (V == V_W4A8G) store_out(p.ep, m, n, v * p.ep.a_scale[m]);
+    else if constexpr (V == V_W4A16G) store_out(p.ep, m, n, v);
     else epilogue_float(p.ep, sa, m, n, v);
 }
 
@@ -150,6 +172,8 @@ __device__ __forceinline__ uint32_t out_bits(const Epilogue& ep, float sa, int64
         y = ((float)acc * ep.a_scale[m]) * ep.w_scale[n];
     } else if constexpr (V == V_W4A8G) {
         y = v * ep.a_scale[m];
+    } else if constexpr (V == V_W4A16G) {
+        y = v;
     } else {
         y = (sa * ep.w_scale[ep.w_per_channel ? n : 0]) * v;
     }

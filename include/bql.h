@@ -20,7 +20,8 @@
  *   - W4A8 per-channel integer linear: int4 weights widened to int8 by a
  *     multiply by 16, int8 per-token activations, int32 accumulation, a
  *     per-channel scale epilogue (QQQ issue #15 "Condition to achieve linear
- *     speedup?").
+ *     speedup?"), and per-group (g128) variants of it and of the weight-only
+ *     int4 linear (the same issue's g128 columns).
  *
  * Conventions (all entry points):
  *   - Every pointer is device memory owned by the caller unless marked
@@ -338,6 +339,25 @@ bql_status bql_w4a8_group_linear(const int8_t* aq, const float* a_scales, const 
                                  const float* w_scales, int64_t M, int64_t N, int64_t K,
                                  int64_t group_size, void* y, bql_dtype ydt, void* ws,
                                  size_t ws_bytes, bql_stream stream);
+
+/* Workspace bytes for bql_w4a16_group_linear at this shape. */
+size_t bql_w4a16_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Per-group weight-only int4 linear (QQQ issue #15: the "awq-g128" and
+ * "marlin-g128" columns, read as fp16 activations, int4 weights with one
+ * scale per output channel n and group g of 128 consecutive k, no zero
+ * point):
+ *   Y[m,n] = sum_g sW[n,g] * sum_{k in g} A[m,k] * W4[n,k],
+ *   each group's sum over exact products in fp32, the groups added in fp32
+ *   in g order.
+ *   a: [M,K] fp16.  w_packed: INT4_GROUP layout (the weight format of
+ *   bql_w4a8_group_linear); w_scales: the scales_out of that prepack
+ *   ([K/128][N] fp32).  group_size must be 128; K a multiple of 128.
+ *   y: [M,N] of ydt = BQL_F16, BQL_BF16 or BQL_F32.  M <= 1048560.
+ *   ws: >= bql_w4a16_linear_workspace_size(M, N, K) bytes. */
+bql_status bql_w4a16_group_linear(const void* a, const void* w_packed, const float* w_scales,
+                                  int64_t M, int64_t N, int64_t K, int64_t group_size, void* y,
+                                  bql_dtype ydt, void* ws, size_t ws_bytes, bql_stream stream);
 
 #ifdef __cplusplus
 }

@@ -166,6 +166,25 @@ def test_w4a8_group_validation(L):
     assert p(A16, 1, 64, 256, 4, A16, 1, A16, A16, None, 0, None) == ERR_DTYPE
 
 
+def test_w4a16_group_validation(L):
+    f = L.bql_w4a16_group_linear
+    ws = L.bql_w4a16_linear_workspace_size(4, 64, 256)
+
+    def call(a=A16, w=A16, s=A16, M=4, N=64, K=256, gs=128, y=A16, ydt=1, work=A16, wsb=ws):
+        return f(a, w, s, M, N, K, gs, y, ydt, work, wsb, None)
+
+    assert call(gs=64) == ERR_ARG
+    assert call(K=200) == ERR_SHAPE      # a multiple of 16 but not of 128
+    assert call(N=60) == ERR_SHAPE
+    assert call(ydt=4) == ERR_DTYPE      # no fp8 output
+    assert call(ydt=6) == ERR_DTYPE
+    assert call(s=None) == ERR_NULL
+    assert call(a=MIS) == ERR_ALIGN
+    assert call(M=-1) == ERR_SHAPE
+    assert call(M=0) == OK
+    assert L.bql_w4a16_linear_workspace_size(0, 64, 256) == 0
+
+
 def test_small_n_shape_rule(L):
     # the fp8 formats take 1 <= N <= 15 (one padded strip); others keep N % 16
     assert L.bql_packed_weight_bytes(8, 4096, 1) == 32 * 2048
