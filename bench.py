@@ -58,8 +58,12 @@ XCDS_MI355X = 8
 # sources the tiled GEMM kernels are built from; a traffic summary is only
 # used while they are unchanged
 KERNEL_SOURCES = ["bit_quantized_linear_amd/csrc/linear.hip",
+                  "bit_quantized_linear_amd/csrc/gemm_exact.hip",
+                  "bit_quantized_linear_amd/csrc/linear_common.h",
                   "bit_quantized_linear_amd/csrc/device.h",
                   "bit_quantized_linear_amd/csrc/kernels.h"]
+EXACT_SIG = "gemm_exact_kernel<"   # the exact fp8 tile kernel at this shape
+FAST_SIG = "gemm_kernel<0,"        # the fp8-MFMA tile kernel
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_m1024_n28672_k4096_hbm_traffic.txt")
 
 
@@ -116,7 +120,7 @@ def summarize_traffic(fetch_dir, write_dir):
         factor = copies[-1] / CALIBRATION_COPY_BYTES
         lines.append(f"  {counter}: calibration copy of {CALIBRATION_COPY_BYTES} B reads {copies[-1]:.1f}"
                      f" counter units -> {1.0 / factor:.2f} B per unit")
-        for tag, sig in (("exact", "gemm_kernel<3,"), ("fast", "gemm_kernel<0,")):
+        for tag, sig in (("exact", EXACT_SIG), ("fast", FAST_SIG)):
             vals = [v for (i, name), v in disp if sig in name.replace(" ", "")]
             if not vals:
                 raise SystemExit(f"no {sig} dispatches in {d}")
@@ -126,7 +130,8 @@ def summarize_traffic(fetch_dir, write_dir):
             lines.append(f"  {tag} GEMM {counter}: {len(vals)} dispatches, {b / 1e6:.1f} MB per launch")
     alg = algorithmic_bytes_gemm(1024, 28672, 4096)
     text = ["# HBM traffic of the dominant GEMM launches, M=1024 N=28672 K=4096",
-            "# (tiled GEMM, exact = f16 MFMA on decoded fp8, fast = fp8 MFMA; pre-quantized A)",
+            "# (exact = gemm_exact_kernel, f16 MFMA on losslessly decoded fp8; fast = gemm_kernel<0,...>,"
+            " fp8 MFMA; pre-quantized A)",
             "commands (repo root; cd /tmp && export TMPDIR=/tmp first, then back):",
             f"  rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python3 bench.py --roofline-only",
             f"  rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o run -- python3 bench.py --roofline-only",
@@ -164,15 +169,16 @@ def summarize_mfma(pmc_dir):
         per[k][r["Counter_Name"]] += float(r["Counter_Value"])
     flops = 2 * 1024 * 28672 * 4096
     lines = ["# Matrix-core counters of the dominant GEMM launches, M=1024 N=28672 K=4096",
-             "# (tiled GEMM, pre-quantized A; exact = f16 MFMA on decoded fp8, fast = fp8 MFMA)",
+             "# (pre-quantized A; exact = gemm_exact_kernel, f16 MFMA on losslessly decoded fp8;"
+             " fast = gemm_kernel<0,...>, fp8 MFMA)",
              "commands (repo root; cd /tmp && export TMPDIR=/tmp first, then back):",
              "  rocprofv3 --pmc " + " ".join(MFMA_COUNTERS)
              + f" -f csv -d {pmc_dir} -o run -- python3 bench.py --roofline-only",
              f"  python3 bench.py --summarize-mfma {pmc_dir}",
              f"source_sha256: {kernel_source_hash()}",
              f"algorithmic flops per launch (2*M*N*K): {flops}"]
-    for tag, sig, mops in (("exact", "gemm_kernel<3,", "SQ_INSTS_VALU_MFMA_MOPS_F16"),
-                           ("fast", "gemm_kernel<0,", "SQ_INSTS_VALU_MFMA_MOPS_F8")):
+    for tag, sig, mops in (("exact", EXACT_SIG, "SQ_INSTS_VALU_MFMA_MOPS_F16"),
+                           ("fast", FAST_SIG, "SQ_INSTS_VALU_MFMA_MOPS_F8")):
         ds = [v for (i, name), v in per.items() if sig in name]
         if not ds:
             raise SystemExit(f"no {sig} dispatches in {pmc_dir}")

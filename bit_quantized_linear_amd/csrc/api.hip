@@ -566,7 +566,9 @@ bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* 
                            bql_dtype ydt, void* ws, size_t ws_bytes, bql_stream stream) {
     CHECK(need_m(M));
     CHECK(need_nk(N, K));
-    if (K > 131072) return fail(BQL_ERR_SHAPE, "K above 131072 could overflow the int32 accumulator");
+    // 16 * |acc| <= 16 * 128 * 8 * K must stay inside int32: K <= 131056
+    // gives at most 2^31 - 2^18 (all products -128 * -8)
+    if (K > 131056) return fail(BQL_ERR_SHAPE, "K above 131056 could overflow the int32 accumulator");
     if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_I32)
         return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16, BQL_F32 or BQL_I32");
     if (M == 0) return ok();

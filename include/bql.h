@@ -318,7 +318,9 @@ size_t bql_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
  *   aq: [M,K] int8; a_scales: M fp32 (may be NULL when ydt = BQL_I32);
  *   w_packed: INT4_CHANNEL layout; w_scales: N fp32 (may be NULL when
  *   ydt = BQL_I32).  y: [M,N] of ydt = BQL_F16, BQL_BF16, BQL_F32 or BQL_I32
- *   (the raw accumulator).  K <= 131072 keeps 16 * acc inside int32. */
+ *   (the raw accumulator).  K <= 131056 keeps 16 * acc inside int32 for
+ *   every int8 code including -128 (at most 2^31 - 2^18); larger K is
+ *   rejected with BQL_ERR_SHAPE. */
 bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* w_packed,
                            const float* w_scales, int64_t M, int64_t N, int64_t K,
                            void* y, bql_dtype ydt, void* ws, size_t ws_bytes,

@@ -272,6 +272,9 @@ def test_w8a16_and_w4a8_validation(L):
     assert g(A16, A16, A16, A16, 1, 64, 64, A16, 4, A16, ws, None) == ERR_DTYPE
     assert g(A16, None, A16, A16, 1, 64, 64, A16, 1, A16, ws, None) == ERR_NULL
     assert g(A16, A16, A16, A16, 1, 64, 131088, A16, 1, A16, ws, None) == ERR_SHAPE
+    # 16 * acc stays inside int32 for K <= 131056 even with -128 codes
+    assert g(A16, A16, A16, A16, 1, 64, 131072, A16, 1, A16, ws, None) == ERR_SHAPE
+    assert g(A16, None, A16, None, 0, 64, 131056, A16, 6, None, 0, None) == OK
     assert g(A16, None, A16, None, 0, 64, 64, A16, 6, None, 0, None) == OK  # raw int32: scales optional
 
 

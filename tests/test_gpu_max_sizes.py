@@ -3,10 +3,11 @@ oracle.
 
 fp8 linear at K = 2^22 (the bql_fp8_linear limit), N = 16: the small-M
 path with fused dynamic quantization (M = 1), the tile path with dynamic
-quantization and with pre-quantized E4M3 A (M = 40).  W4A8 at K = 131072
-(the limit that keeps 16 * acc inside int32), int32 accumulators compared
-bit for bit, with every product at its largest magnitude of one sign so
-that the sum reaches its extreme.  Per-group W4A8 at K = 16384 (128 groups,
+quantization and with pre-quantized E4M3 A (M = 40).  W4A8 at K = 131056
+(the limit that keeps 16 * acc inside int32 for every int8 code, -128
+included), int32 accumulators compared bit for bit, with every product of
+the first row and channel at the largest magnitude, -128 * -8, so that the
+sum reaches its extreme.  Per-group W4A8 at K = 16384 (128 groups,
 the limit of the staged scales).  W8A16 at K = 2^24, the limit of the
 weight formats.  Both RMSNorm quantizers at M = 2^22, the row limit.
 """
@@ -23,7 +24,7 @@ import bit_quantized_linear_amd as bql
 pytestmark = pytest.mark.gpu
 
 K_FP8 = 1 << 22
-K_W4A8 = 131072
+K_W4A8 = 131056
 K_GROUP = 16384
 
 
@@ -61,20 +62,20 @@ def test_fp8_linear_max_k_prequantized(fp8_case):
 
 @pytest.mark.parametrize("M", [1, 40])
 def test_w4a8_max_k_extreme_sum(M):
-    # most products are -127 * -8 = +1016: a row with all of them would give
-    # acc = 1016 * K, i.e. 16 * acc = 2^31 - 2^24, the top of the int32 range
-    # the int8 MMA works in; a few sign changes make the rows differ
+    # row 0 of A and channel 0 of W hold -128 and -8 throughout: acc[0, 0] =
+    # 1024 * K, i.e. 16 * acc = 2^31 - 2^18, the top of the int32 range the
+    # int8 MMA works in; sign changes elsewhere make the other entries differ
     N = 16
     w4 = np.full((N, K_W4A8), -8, dtype=np.int8)
-    aq = np.full((M, K_W4A8), -127, dtype=np.int8)
-    aq[:, ::7] = 127
+    aq = np.full((M, K_W4A8), -128, dtype=np.int8)
+    aq[1:, ::7] = 127
     w4[1::2, ::5] = 7
     pw = bql.prepack_weight(torch.from_numpy(wl.pack_int4(w4).reshape(N, K_W4A8 // 2)).to(DEV),
                             "int4_channel", scales=torch.ones(N, dtype=torch.float16, device=DEV))
     acc = bql.w4a8_linear(dev(aq), None, pw, out_dtype=torch.int32)
     torch.cuda.synchronize()
     ref = oracle.w4a8_acc(aq, w4)
-    assert np.abs(ref).max() < 2 ** 31 // 16, "the case must stay inside the documented range"
+    assert ref[0, 0] * 16 == 2 ** 31 - 2 ** 18, "the case must reach the documented extreme"
     assert np.array_equal(host(acc).astype(np.int64), ref), f"W4A8 K={K_W4A8} M={M} accumulators differ"
 
 
