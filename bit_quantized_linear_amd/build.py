@@ -30,13 +30,22 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The per-group W4A16 tile kernel folds each
+# matrix-core result into fp32 accumulators with vector instructions, so its
+# MFMA results must land in ordinary vector registers (the compiler's default
+# there puts them in the accumulation registers and copies every value out).
+EXTRA_FLAGS = {
+    "gemm_w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

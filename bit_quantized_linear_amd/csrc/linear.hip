@@ -988,8 +988,8 @@ constexpr int FUSED_M = 4;                 // small-M fp8 calls that quantize A 
 constexpr int64_t FUSED_LDS = 48 * 1024;   // bytes of A codes a fused block may stage
 
 bool use_small_m(int variant, int64_t M, int64_t N, int64_t K) {
-    (void)N; (void)K;
-    return variant == V_W8A16 || variant == V_W4A16G || M <= SMALL_M;
+    if (variant == V_W4A16G) return M <= SMALL_M || !w4a16_tile_fits(M, N, K);
+    return variant == V_W8A16 || M <= SMALL_M;
 }
 
 struct GemvPlan {
@@ -1204,6 +1204,10 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
             case V_W4A16G: return run_gemv<V_W4A16G, false>(p, stream);
             default: return run_gemv<V_W4A8, false>(p, stream);
         }
+    }
+    if (args.variant == V_W4A16G) {
+        p.KT = (args.K + TILE_K - 1) / TILE_K;
+        return launch_gemm_w4a16(p, stream);
     }
     if (args.a_rowmajor && !reads_rowmajor_a(args.variant, args.M, args.N, args.K))
         return hipErrorInvalidValue;  // this shape's tile kernel takes packed A

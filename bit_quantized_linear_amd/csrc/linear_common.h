@@ -228,4 +228,10 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t nbm, int64_t nbn,
 // tile per wave); defined in gemm_exact.hip.
 hipError_t launch_gemm_exact(const LinParams& p, hipStream_t stream);
 
+// Launch of the per-group W4A16 tile kernel (128 x 256 blocks, one 128 x 64
+// output tile per wave); defined in gemm_w4a16.hip.  w4a16_tile_fits tells
+// whether a shape is inside that kernel's offset range.
+hipError_t launch_gemm_w4a16(const LinParams& p, hipStream_t stream);
+bool w4a16_tile_fits(int64_t M, int64_t N, int64_t K);
+
 }  // namespace bql

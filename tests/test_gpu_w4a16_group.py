@@ -50,8 +50,11 @@ def test_w4a16_group_workload(M, KN):
     assert_close(host_f64(y)[rows], ref, f"W4A16 g128 M={M} K=N={KN}")
 
 
+# M above 16 runs the tile kernel (128 x 256 blocks): partial row blocks
+# (77, 300, 130), a column block with waves wholly past N (272), one and
+# two k-tiles (the pipeline's shortest runs) and odd k-tile counts (384)
 @pytest.mark.parametrize("M,N,K", [(77, 1040, 384), (3, 16, 128), (300, 272, 1280), (16, 2064, 4096),
-                                   (1, 4096, 14336)])
+                                   (1, 4096, 14336), (40, 512, 128), (130, 4096, 256), (17, 784, 640)])
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16, torch.float32])
 def test_w4a16_group_ragged(M, N, K, out):
     g = wl.rng(94, M, N, K)
@@ -65,7 +68,7 @@ def test_w4a16_group_ragged(M, N, K, out):
     assert_close(host_f64(y), ref, f"W4A16 g128 M={M} N={N} K={K} {out}")
 
 
-@pytest.mark.parametrize("M", [1, 8, 40])
+@pytest.mark.parametrize("M", [1, 8, 40, 300])
 def test_w4a16_group_exact_small_integers(M):
     # every nibble value -8..7 in every byte position, integer activations
     # and power-of-two group scales: all fp32 partial sums are exact, so the
