@@ -655,7 +655,7 @@ bql_status bql_w4a8_group_linear(const int8_t* aq, const float* a_scales, const 
 
 size_t bql_w4a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return align256(bql::small_m_ws_bytes(M, N, K, bql::V_W4A16G));
+    return align256(bql::w4a16_ws_bytes(M, N, K));
 }
 
 bql_status bql_w4a16_group_linear(const void* a, const void* w_packed, const float* w_scales,

@@ -56,11 +56,11 @@ static_assert(QLD + 2 * QFN < 64, "vmcnt range");
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Writes the wave's staged 128 x 64 tile (OUT bits, QEPI_ROW bytes per row)
-// to Y with 16-byte stores.  N is a multiple of 16, so a store's columns
+// to y (row stride ldy elements) with 16-byte stores.  N is a multiple of 16, so a store's columns
 // lie all inside or all outside N.
 template <int OUT>
-__device__ __forceinline__ void copy_out(const LinParams& p, const uint8_t* band, int64_t m0,
-                                         int64_t col0, int lane) {
+__device__ __forceinline__ void copy_out(const LinParams& p, uint8_t* y, int64_t ldy, const uint8_t* band,
+                                         int64_t m0, int64_t col0, int lane) {
     constexpr int ESZ = OUT == OUT_F32 ? 4 : 2;
     constexpr int CHUNKS = QFN * 16 * ESZ / 16, ITERS = QM * CHUNKS / 64;
 #pragma unroll
@@ -68,7 +68,7 @@ __device__ __forceinline__ void copy_out(const LinParams& p, const uint8_t* band
         const int q = lane + 64 * it, row = q / CHUNKS, ch = q % CHUNKS;
         const int64_t m = m0 + row, n = col0 + ch * (16 / ESZ);
         const u4 v = *(const u4*)(band + row * QEPI_ROW + ch * 16);
-        if (m < p.M && n < p.N) *(u4*)((uint8_t*)p.ep.y + (m * p.ep.ldy + n) * ESZ) = v;
+        if (m < p.M && n < p.N) *(u4*)(y + (m * ldy + n) * ESZ) = v;
     }
 }
 
@@ -118,7 +118,9 @@ void gemm_w4a16_kernel(LinParams p) {
     bm = __builtin_amdgcn_readfirstlane((int)bm);
     bn = __builtin_amdgcn_readfirstlane((int)bn);
     const int64_t m0 = bm * QM, col0 = bn * QN + wave * QFN * 16;
-    const int KT = (int)p.KT;
+    // this block's k range: split blockIdx.y of the K dimension
+    const int kt0 = (int)(blockIdx.y * p.kt_per_split);
+    const int KT = (int)(p.KT - kt0 < p.kt_per_split ? p.KT - kt0 : p.kt_per_split);
     const int64_t K2 = p.K * 2;  // bytes per A row
 
     // Descriptors: the block's A rows (rows past M read as zero), the wave's
@@ -147,7 +149,7 @@ void gemm_w4a16_kernel(LinParams p) {
     const uint32_t avoff = (uint32_t)(ar * K2 + (((lane & 15) ^ ar) * 16));
     auto dma_a = [&](int kt) __attribute__((always_inline)) {
         uint8_t* dst = lds + (kt % QS) * QSTAGE + wave * 1024;
-        const int ktc = kt < KT ? kt : KT - 1;
+        const int ktc = kt0 + (kt < KT ? kt : KT - 1);
 #pragma unroll
         for (int u = 0; u < QLD; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + u * 4096), 16,
@@ -155,7 +157,7 @@ void gemm_w4a16_kernel(LinParams p) {
     };
     // Weight tile of strip j, k-tile kt: the lane's 16 packed bytes.
     auto load_b = [&](int kt, u4 (&b)[QFN]) __attribute__((always_inline)) {
-        const int ktc = kt < KT ? kt : KT - 1;
+        const int ktc = kt0 + (kt < KT ? kt : KT - 1);
 #pragma unroll
         for (int j = 0; j < QFN; ++j) {
             const int js = j < nbs ? j : (int)nbs - 1;
@@ -172,7 +174,7 @@ void gemm_w4a16_kernel(LinParams p) {
         scol[j] = (int)((n < p.N ? n : p.N - 1) * 4);
     }
     auto load_s = [&](int kt, float (&s)[QFN]) __attribute__((always_inline)) {
-        const int ktc = kt < KT ? kt : KT - 1;
+        const int ktc = kt0 + (kt < KT ? kt : KT - 1);
 #pragma unroll
         for (int j = 0; j < QFN; ++j)
             s[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, scol[j], (int)(ktc * p.N * 4), 0));
@@ -310,8 +312,15 @@ void gemm_w4a16_kernel(LinParams p) {
                     else *(uint16_t*)d = (uint16_t)f32_to_bf16_bits(v);
                 }
         __builtin_amdgcn_wave_barrier();
-        copy_out<OUT>(p, band, m0, col0, lane);
+        if (p.splits > 1)  // fp32 partial sums of this split, summed by the split-K reduce
+            copy_out<OUT>(p, (uint8_t*)p.partial + (int64_t)blockIdx.y * p.M * p.N * 4, p.N, band, m0, col0, lane);
+        else
+            copy_out<OUT>(p, (uint8_t*)p.ep.y, p.ep.ldy, band, m0, col0, lane);
     };
+    if (p.splits > 1) {
+        epilogue(std::integral_constant<int, OUT_F32>{});
+        return;
+    }
     switch (p.ep.ydt) {
         case OUT_F16: epilogue(std::integral_constant<int, OUT_F16>{}); break;
         case OUT_BF16: epilogue(std::integral_constant<int, OUT_BF16>{}); break;
@@ -340,8 +349,31 @@ hipError_t launch_gemm_w4a16(const LinParams& p, hipStream_t stream) {
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
     const int64_t blocks = ((p.M + QM - 1) / QM) * ((p.N + QN - 1) / QN);
-    gemm_w4a16_kernel<<<(unsigned)blocks, 64 * QW, QLDS_ALL, stream>>>(p);
+    gemm_w4a16_kernel<<<dim3((unsigned)blocks, (unsigned)p.splits), 64 * QW, QLDS_ALL, stream>>>(p);
     return hipGetLastError();
+}
+
+int w4a16_tile_splits(int64_t M, int64_t N, int64_t K) {
+    // One block per CU at a time: a launch of s splits takes
+    // ceil(blocks * s / CUs) rounds of ceil(KT / s) k-tiles.  The fp32
+    // partial sums are written and read back once each (8 bytes per output
+    // and split); measured, one k-tile of a block takes about as long as the
+    // chip moves 9 MB.  The split count minimizes the sum, in k-tile times,
+    // keeping 4+ k-tiles per split.
+    constexpr int64_t CUS = 256;
+    constexpr double BYTES_PER_KTILE = 9e6;
+    const int64_t tiles = ((M + QM - 1) / QM) * ((N + QN - 1) / QN), kt = K / TILE_K;
+    int best = 1;
+    double best_cost = (double)((tiles + CUS - 1) / CUS) * kt;
+    for (int s = 2; s <= 8 && kt / s >= 4; ++s) {
+        const double cost = (double)((tiles * s + CUS - 1) / CUS) * ((kt + s - 1) / s) +
+                            (double)s * M * N * 8 / BYTES_PER_KTILE;
+        if (cost < best_cost) {
+            best = s;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 }  // namespace bql

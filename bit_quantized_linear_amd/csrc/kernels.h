@@ -111,6 +111,9 @@ bool fused_small_m(int64_t M, int64_t N, int64_t K);
 
 // Workspace bytes the small-M (split-K) path may use at this shape.
 size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant);
+// Workspace bytes of the per-group W4A16 linear at this shape (split-K
+// partial sums of the streaming or the tile kernel).
+size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K);
 // Which path runs: true for the streaming small-M kernels.
 bool use_small_m(int variant, int64_t M, int64_t N, int64_t K);
 // Whether the kernel that runs at this shape reads 8-bit A row-major at full

@@ -1014,6 +1014,13 @@ static GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
     return pl;
 }
 
+size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    if (use_small_m(V_W4A16G, M, N, K)) return small_m_ws_bytes(M, N, K, V_W4A16G);
+    const int s = w4a16_tile_splits(M, N, K);
+    const int64_t KT = K / TILE_K, per = (KT + s - 1) / s, splits = (KT + per - 1) / per;
+    return splits > 1 ? (size_t)splits * M * N * 4 : 0;
+}
+
 size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant) {
     if (!use_small_m(variant, M, N, K) || M > SMALL_M) return 0;
     GemvPlan pl = plan_gemv(M, N, K);
@@ -1207,7 +1214,14 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
     }
     if (args.variant == V_W4A16G) {
         p.KT = (args.K + TILE_K - 1) / TILE_K;
-        return launch_gemm_w4a16(p, stream);
+        const int s = w4a16_tile_splits(args.M, args.N, args.K);
+        p.kt_per_split = (p.KT + s - 1) / s;
+        p.splits = (int)((p.KT + p.kt_per_split - 1) / p.kt_per_split);
+        hipError_t e = launch_gemm_w4a16(p, stream);
+        if (e != hipSuccess || p.splits == 1) return e;
+        const int64_t total = p.M * p.N;
+        splitk_reduce_kernel<V_W4A16G><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
+        return hipGetLastError();
     }
     if (args.a_rowmajor && !reads_rowmajor_a(args.variant, args.M, args.N, args.K))
         return hipErrorInvalidValue;  // this shape's tile kernel takes packed A

@@ -233,5 +233,8 @@ hipError_t launch_gemm_exact(const LinParams& p, hipStream_t stream);
 // whether a shape is inside that kernel's offset range.
 hipError_t launch_gemm_w4a16(const LinParams& p, hipStream_t stream);
 bool w4a16_tile_fits(int64_t M, int64_t N, int64_t K);
+// K splits of the tile kernel at this shape (fp32 partials in the workspace,
+// then the split-K reduce); 1 when every CU already has a block.
+int w4a16_tile_splits(int64_t M, int64_t N, int64_t K);
 
 }  // namespace bql
