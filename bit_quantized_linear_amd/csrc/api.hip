@@ -1,6 +1,7 @@
 // C ABI of the library: argument checking on the host, then launches.
 // Nothing here allocates or synchronizes; see include/bql.h for the
 // contract of every entry point.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
@@ -312,8 +313,8 @@ bql_status bql_unpack_weight(const void* packed, int64_t N, int64_t K, bql_wfmt 
 // tiles][split-K partials]
 size_t bql_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K)) +
-           align256(bql::small_m_ws_bytes(M, N, K, bql::V_FP8));
+    const size_t split = std::max(bql::split_ws_bytes(M, N, K, bql::V_FP8), bql::split_ws_bytes(M, N, K, bql::V_FP8X));
+    return bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K)) + align256(split);
 }
 
 // N < 16: the small-N kernel reads A where it is (E4M3 codes, or fp16 /
@@ -402,7 +403,7 @@ static bql_status run_fp8_linear(const void* a, bql_dtype adt, float* a_scale, c
         la.xdt = adt;
         la.scale_out = a_scale;
         la.scale_ws = (float*)(wsb + 4096);
-        return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+        return hip_status(bql::launch_linear(la, part, bql::split_ws_bytes(M, N, K, variant), s));
     }
     const float* sa = a_scale;
     // pre-quantized A is read row-major where it is by the kernels that read
@@ -430,7 +431,7 @@ static bql_status run_fp8_linear(const void* a, bql_dtype adt, float* a_scale, c
     la.w_scale = w_scale;
     la.w_per_channel = w_per_channel;
     la.out_scale = output_scale;
-    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+    return hip_status(bql::launch_linear(la, part, bql::split_ws_bytes(M, N, K, variant), s));
 }
 
 bql_status bql_fp8_linear(const void* a, bql_dtype adt, float* a_scale, const void* w_packed,
@@ -512,17 +513,17 @@ bql_status bql_fp8_linear_static(const void* a, bql_dtype adt, const float* a_sc
         la.fused = 1;
         la.xdt = adt;
         la.given_scale = a_scale;
-        return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+        return hip_status(bql::launch_linear(la, part, bql::split_ws_bytes(M, N, K, variant), s));
     }
     hipError_t e = bql::launch_quant_static_packed(a, adt, M, K, a_scale, aq, s);
     if (e != hipSuccess) return hip_status(e);
     la.a = aq;
-    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, variant), s));
+    return hip_status(bql::launch_linear(la, part, bql::split_ws_bytes(M, N, K, variant), s));
 }
 
 size_t bql_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return align256(bql::small_m_ws_bytes(M, N, K, bql::V_W8A16));
+    return align256(bql::split_ws_bytes(M, N, K, bql::V_W8A16));
 }
 
 bql_status bql_w8a16_linear(const void* a, const void* w_packed, const float* w_scales, int64_t M,
@@ -558,7 +559,7 @@ bql_status bql_w8a16_linear(const void* a, const void* w_packed, const float* w_
 // W4A8 workspace: [Aq, packed operand tiles][split-K partials]
 size_t bql_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return align256(bql::packed_act_bytes(M, K)) + align256(bql::small_m_ws_bytes(M, N, K, bql::V_W4A8));
+    return align256(bql::packed_act_bytes(M, K)) + align256(bql::split_ws_bytes(M, N, K, bql::V_W4A8));
 }
 
 bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* w_packed,
@@ -602,7 +603,7 @@ bql_status bql_w4a8_linear(const int8_t* aq, const float* a_scales, const void* 
     la.w_per_channel = 1;
     la.out_scale = nullptr;
     char* part = (char*)ws + align256(bql::packed_act_bytes(M, K));
-    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_W4A8),
+    return hip_status(bql::launch_linear(la, part, bql::split_ws_bytes(M, N, K, bql::V_W4A8),
                                          (hipStream_t)stream));
 }
 
@@ -649,7 +650,7 @@ bql_status bql_w4a8_group_linear(const int8_t* aq, const float* a_scales, const 
     la.w_per_channel = 1;
     la.out_scale = nullptr;
     char* part = (char*)ws + align256(bql::packed_act_bytes(M, K));
-    return hip_status(bql::launch_linear(la, part, bql::small_m_ws_bytes(M, N, K, bql::V_W4A8G),
+    return hip_status(bql::launch_linear(la, part, bql::split_ws_bytes(M, N, K, bql::V_W4A8G),
                                          (hipStream_t)stream));
 }
 

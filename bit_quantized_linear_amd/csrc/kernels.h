@@ -114,6 +114,9 @@ size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant);
 // Workspace bytes of the per-group W4A16 linear at this shape (split-K
 // partial sums of the streaming or the tile kernel).
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K);
+// Workspace bytes of a linear's split-K partial sums at this shape, for the
+// kernel that runs it (streaming or tile): 0 when K is not split.
+size_t split_ws_bytes(int64_t M, int64_t N, int64_t K, int variant);
 // Which path runs: true for the streaming small-M kernels.
 bool use_small_m(int variant, int64_t M, int64_t N, int64_t K);
 // Whether the kernel that runs at this shape reads 8-bit A row-major at full

@@ -400,6 +400,31 @@ __device__ __forceinline__ int a_tile_offset(const ATiles& t, int strip, int h, 
     return (strip * t.KT + kt) * 2048 + h * 1024 + lane * 16;
 }
 
+// One 16 x 16 accumulator tile's raw sums (fp32, or the int32 of the W4A8
+// kernels) into split blockIdx.y's partial buffer [M][N]; rows past M and
+// columns past N are skipped.
+template <int V>
+__device__ __forceinline__ void store_partial_tile(const LinParams& p, const typename VT<V>::Acc& a,
+                                                   int64_t r0, int64_t c0, int lane) {
+    using E = typename VT<V>::E;
+    E* part = (E*)p.partial + (int64_t)blockIdx.y * p.M * p.N;
+    const int64_t n = c0 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t m = r0 + 4 * (lane >> 4) + r;
+        if (m < p.M && n < p.N) part[m * p.N + n] = a[r];
+    }
+}
+
+template <int V, int FM, int FN>
+__device__ __forceinline__ void store_partials(const LinParams& p, const typename VT<V>::Acc (&acc)[FM][FN],
+                                               int64_t r0, int64_t c0, int lane) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) store_partial_tile<V>(p, acc[i][j], r0 + i * 16, c0 + j * 16, lane);
+}
+
 template <int V, int BM, int BN, int WM, int WN, int S>
 struct GemmCfg {
     static constexpr int NW = WM * WN;
@@ -595,7 +620,9 @@ __attribute__((amdgpu_waves_per_eu(V == V_W4A8G ? 2 : 1, 8))) void gemm_pipe_ker
     const int64_t m0 = bm * BM, n0 = bn * BN;
     const int64_t mt0 = m0 / 16, nt0 = n0 / 16;
     const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
-    const int KT = (int)p.KT;
+    // k-tiles kt0 .. kt0 + KT - 1 (split blockIdx.y of K); KS strides strips
+    const int KS = (int)p.KT, kt0 = (int)(blockIdx.y * p.kt_per_split);
+    const int KT = (int)(p.KT - kt0 < p.kt_per_split ? p.KT - kt0 : p.kt_per_split);
 
     const int64_t a_strips = mtiles - mt0 < BM / 16 ? mtiles - mt0 : BM / 16;
     const int64_t b_strips = ntiles - nt0 < BN / 16 ? ntiles - nt0 : BN / 16;
@@ -610,7 +637,7 @@ __attribute__((amdgpu_waves_per_eu(V == V_W4A8G ? 2 : 1, 8))) void gemm_pipe_ker
 #pragma unroll
         for (int i = 0; i < C::A_LD / NW; ++i) {
             const int slot = wave + NW * i, sub = slot >> 1, h = slot & 1;
-            const int off = (sub * KT + kt) * 2048 + h * 1024 + lane * 16;
+            const int off = (sub * KS + kt0 + kt) * 2048 + h * 1024 + lane * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + slot * 1024), 16, off, 0,
                                                      0, 0);
         }
@@ -618,8 +645,8 @@ __attribute__((amdgpu_waves_per_eu(V == V_W4A8G ? 2 : 1, 8))) void gemm_pipe_ker
         for (int i = 0; i < C::B_LD / NW; ++i) {
             const int slot = wave + NW * i;
             int off;
-            if constexpr (BT == 2048) off = ((slot >> 1) * KT + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
-            else off = (slot * KT + kt) * 1024 + lane * 16;
+            if constexpr (BT == 2048) off = ((slot >> 1) * KS + kt0 + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
+            else off = (slot * KS + kt0 + kt) * 1024 + lane * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + C::A_BYTES + slot * 1024),
                                                      16, off, 0, 0, 0);
         }
@@ -706,7 +733,7 @@ __attribute__((amdgpu_waves_per_eu(V == V_W4A8G ? 2 : 1, 8))) void gemm_pipe_ker
         float* g = (float*)(lds + C::LDS);
         for (int q = tid; q < KT * BN; q += 64 * NW) {
             const int64_t n = n0 + q % BN;
-            g[q] = n < p.N ? p.ep.w_scale[(int64_t)(q / BN) * p.N + n] * 0.0625f : 0.0f;  // scale / 16
+            g[q] = n < p.N ? p.ep.w_scale[(int64_t)(kt0 + q / BN) * p.N + n] * 0.0625f : 0.0f;  // scale / 16
         }
         __syncthreads();
     }
@@ -739,9 +766,14 @@ __attribute__((amdgpu_waves_per_eu(V == V_W4A8G ? 2 : 1, 8))) void gemm_pipe_ker
         compute(f0, kt);
     }
 
-    // ---- epilogue (as gemm_kernel)
+    // ---- epilogue (as gemm_kernel); with K split over blocks, this split's
+    // raw sums go to its partial buffer for the split-K reduce
     __syncthreads();
     wait_vmcnt<0>();
+    if (p.splits > 1) {
+        store_partials<V, FM, FN>(p, acc, m0 + wm * FM * 16, n0 + wn * FN * 16, lane);
+        return;
+    }
     const float sa = (V == V_FP8 || V == V_FP8X) ? *p.ep.a_scale : 1.0f;
     const int esz = out_size(p.ep.ydt);
     uint8_t* scratch = lds + wave * C::EPI_WAVE;
@@ -815,7 +847,9 @@ __global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
     tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, bm, bn);
     const int64_t m0 = bm * BM, n0 = bn * BN;
     const int64_t nt0 = n0 / 16, ntiles = p.N / 16;
-    const int KT = (int)p.KT;
+    // k-tiles kt0 .. kt0 + KT - 1 (split blockIdx.y of K); KS strides strips
+    const int KS = (int)p.KT, kt0 = (int)(blockIdx.y * p.kt_per_split);
+    const int KT = (int)(p.KT - kt0 < p.kt_per_split ? p.KT - kt0 : p.kt_per_split);
 
     // A packed or row-major (see ATiles)
     const int64_t b_strips = ntiles - nt0 < BN / 16 ? ntiles - nt0 : BN / 16;
@@ -829,13 +863,13 @@ __global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
         for (int i = 0; i < C::A_LD / NW; ++i) {
             const int slot = wave + NW * i;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(at.rsrc, (lds_ptr_t)(base + slot * 1024), 16,
-                                                     a_tile_offset(at, slot >> 1, slot & 1, kt, lane),
+                                                     a_tile_offset(at, slot >> 1, slot & 1, kt0 + kt, lane),
                                                      0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < C::B_LD / NW; ++i) {
             const int slot = wave + NW * i;
-            const int off = ((slot >> 1) * KT + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
+            const int off = ((slot >> 1) * KS + kt0 + kt) * 2048 + (slot & 1) * 1024 + lane * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + C::A_BYTES + slot * 1024),
                                                      16, off, 0, 0, 0);
         }
@@ -938,6 +972,19 @@ __global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
                         acc[i][j][r] += in[(((i % (FM / 2)) * FN + j) * 4 + r) * 64 + lane];
     }
     __syncthreads();
+
+    // with K split over blocks, this split's raw sums (each group's half of
+    // the row tiles) go to its partial buffer for the split-K reduce
+    if (p.splits > 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            if ((i < FM / 2) != low) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                store_partial_tile<V_FP8X>(p, acc[i][j], m0 + (wm * FM + i) * 16, n0 + (wn * FN + j) * 16, lane);
+        }
+        return;
+    }
 
     // ---- epilogue: per 16-row band, values staged in LDS, 16-byte stores
     const float sa = *p.ep.a_scale;
@@ -1096,7 +1143,8 @@ static hipError_t launch_gemm_pipe(const LinParams& p, hipStream_t stream) {
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
     const int64_t blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    gemm_pipe_kernel<V, BM, BN, WM, WN, S><<<(unsigned)blocks, 64 * WM * WN, lds, stream>>>(p);
+    gemm_pipe_kernel<V, BM, BN, WM, WN, S><<<dim3((unsigned)blocks, (unsigned)p.splits), 64 * WM * WN, lds,
+                                             stream>>>(p);
     return hipGetLastError();
 }
 
@@ -1115,7 +1163,8 @@ static hipError_t launch_gemm_ks(const LinParams& p, hipStream_t stream) {
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
     const int64_t blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    gemm_ks_kernel<BM, BN, WM, WN, S><<<(unsigned)blocks, 128 * WM * WN, C::LDS, stream>>>(p);
+    gemm_ks_kernel<BM, BN, WM, WN, S><<<dim3((unsigned)blocks, (unsigned)p.splits), 128 * WM * WN, C::LDS,
+                                        stream>>>(p);
     return hipGetLastError();
 }
 
@@ -1143,8 +1192,70 @@ bool reads_rowmajor_a(int variant, int64_t M, int64_t N, int64_t K) {
     return use_small_m(variant, M, N, K) || uses_ks(variant, M, N);
 }
 
+// K splits of the 128 x 128 tile kernels that take them (the exact k-split
+// kernel, the register-prefetch kernel: fast fp8 with at most one tile per
+// CU, W4A8 per channel and per group).  With few output tiles most CUs idle
+// while each block walks all of K (M = 128 and 256 at these N), so K is split
+// over blocks whose raw sums go to fp32 / int32 partials and the split-K
+// reduce.  Cost in k-tile times of one block: ceil(blocks / CUs) rounds of
+// ceil(KT / s) k-tiles, plus the partials' write and read (8 bytes per
+// output and split; a 128 x 128 block's k-tile takes about as long as the
+// chip moves 4 MB).  At most 8 splits of 4+ k-tiles.
+static bool tile_splittable(int variant, int64_t M, int64_t N) {
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (variant == V_FP8X) return t256 < EXACT_BIG_TILES && uses_ks(variant, M, N);
+    if (variant == V_FP8) return t128 <= CUS;
+    return variant == V_W4A8 || variant == V_W4A8G;
+}
+
+static int tile_splits(int variant, int64_t M, int64_t N, int64_t K) {
+    if (use_small_m(variant, M, N, K) || !tile_splittable(variant, M, N)) return 1;
+    constexpr double BYTES_PER_KTILE = 4e6;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128), kt = (K + TILE_K - 1) / TILE_K;
+    int best = 1;
+    double best_cost = (double)((tiles + CUS - 1) / CUS) * kt;
+    for (int sp = 2; sp <= MAX_SPLITS && kt / sp >= 4; ++sp) {
+        const double cost = (double)((tiles * sp + CUS - 1) / CUS) * ((kt + sp - 1) / sp) +
+                            (double)sp * M * N * 8 / BYTES_PER_KTILE;
+        if (cost < best_cost) {
+            best = sp;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+size_t split_ws_bytes(int64_t M, int64_t N, int64_t K, int variant) {
+    if (variant == V_W4A16G) return w4a16_ws_bytes(M, N, K);
+    if (use_small_m(variant, M, N, K)) return small_m_ws_bytes(M, N, K, variant);
+    const int sp = tile_splits(variant, M, N, K);
+    const int64_t kt = (K + TILE_K - 1) / TILE_K, per = (kt + sp - 1) / sp, n = (kt + per - 1) / per;
+    return n > 1 ? (size_t)n * M * N * 4 : 0;
+}
+
 template <int V>
-static hipError_t run_gemm(const LinParams& p, hipStream_t stream) {
+static hipError_t run_gemm_kernel(const LinParams& p, hipStream_t stream);
+
+// The tile kernel chosen by run_gemm_kernel, with K split over blocks when
+// tile_splits says so (then the split-K reduce applies the epilogue).
+template <int V>
+static hipError_t run_gemm(const LinParams& p0, hipStream_t stream) {
+    LinParams p = p0;
+    const int sp = tile_splits(V, p.M, p.N, p.K);
+    if (sp > 1) {
+        p.kt_per_split = (p.KT + sp - 1) / sp;
+        p.splits = (int)((p.KT + p.kt_per_split - 1) / p.kt_per_split);
+    }
+    hipError_t e = run_gemm_kernel<V>(p, stream);
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int64_t total = p.M * p.N;
+    splitk_reduce_kernel<V><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+template <int V>
+static hipError_t run_gemm_kernel(const LinParams& p, hipStream_t stream) {
     const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
     if constexpr (V == V_FP8X) {
