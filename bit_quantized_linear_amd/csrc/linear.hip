@@ -1262,7 +1262,9 @@ static hipError_t run_gemm_kernel(const LinParams& p, hipStream_t stream) {
         // many 256x256 tiles: the 128x128-per-wave kernel (half the
         // conversions per MFMA of the 64x64-per-wave kernels)
         if (t256 >= EXACT_BIG_TILES) return launch_gemm_exact(p, stream);
-        if (uses_ks(V, p.M, p.N)) return launch_gemm_ks<128, 128, 2, 2, 2>(p, stream);
+        // at most one 128x128 tile per CU: a four-stage ring, so that each
+        // k-tile's DMA has three k-tiles of compute to land behind
+        if (uses_ks(V, p.M, p.N)) return launch_gemm_ks<128, 128, 2, 2, 4>(p, stream);
         // Two blocks share a CU, so the busiest CU carries ceil(tiles / CUs)
         // tiles: 128x96 tiles win where they even that out (M = 1024, N =
         // 6144: 384 tiles of 128 columns leave half the CUs with two, 512
@@ -1272,12 +1274,15 @@ static hipError_t run_gemm_kernel(const LinParams& p, hipStream_t stream) {
             return launch_gemm<V, 128, 96, 2, 2, 2>(p, stream);
         return launch_gemm<V, 128, 128, 2, 2, 2>(p, stream);
     } else if constexpr (V == V_FP8) {
-        if (t128 <= CUS) return launch_gemm_pipe<V, 128, 128, 4, 2, 3>(p, stream);
+        if (t128 <= CUS) return launch_gemm_pipe<V, 128, 128, 4, 2, 4>(p, stream);
         if (t256 >= 3 * CUS / 2) return launch_gemm<V, 256, 256, 4, 4, 2>(p, stream);
         return launch_gemm<V, 128, 128, 2, 4, 2>(p, stream);
     } else if constexpr (V == V_W4A8G) {  // best at every K = N in 4096..8192 measured
+        // at most one tile per CU (a block per CU at a time): a four-stage ring
+        if (t128 * p.splits <= CUS) return launch_gemm_pipe<V, 128, 128, 2, 2, 4>(p, stream);
         return launch_gemm_pipe<V, 128, 128, 2, 2, 2>(p, stream);
     } else {  // per-channel W4A8: best at every K = N in 4096..8192 measured
+        if (t128 * p.splits <= CUS) return launch_gemm_pipe<V, 128, 128, 2, 4, 4>(p, stream);
         return launch_gemm_pipe<V, 128, 128, 2, 4, 2>(p, stream);
     }
 }
