@@ -806,6 +806,8 @@ def main():
                     help="only the dominant-kernel launches (for a rocprofv3 run of that kernel)")
     ap.add_argument("--rmsnorm-only", action="store_true",
                     help="only the fused RMSNorm + quantization leg (for a rocprofv3 run of it)")
+    ap.add_argument("--w4a8-only", action="store_true",
+                    help="only the per-channel W4A8 leg (for a rocprofv3 run of it)")
     ap.add_argument("--w4a8-group-only", action="store_true",
                     help="only the per-group W4A8 and W4A16 legs (for a rocprofv3 run of them)")
     ap.add_argument("--small-n-only", action="store_true",
@@ -833,6 +835,9 @@ def main():
     if args.rmsnorm_only:
         print(json.dumps({"rmsnorm_quant": bench_rmsnorm_quant(bql, dev, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.w4a8_only:
+        print(json.dumps({"w4a8": bench_w4a8(bql, dev, args.steps, args.warmup)}), flush=True)
         return
     if args.w4a8_group_only:
         print(json.dumps({"w4a8_group": bench_int4_group(bql, dev, args.steps, args.warmup),
