@@ -138,10 +138,15 @@ __global__ __launch_bounds__(64 * XW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_exact_kernel(LinParams p) {
     constexpr int BN = 32 * FN;  // block columns
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index and the tile coordinates (whose 64-bit divisions run on
+    // the vector ALU) are uniform: read them as such, so that the DMA
+    // addresses built from them stay scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     int64_t bm, bn;
     tile_coords(blockIdx.x, (p.M + XB - 1) / XB, (p.N + BN - 1) / BN, bm, bn);
+    bm = __builtin_amdgcn_readfirstlane((int)bm);
+    bn = __builtin_amdgcn_readfirstlane((int)bn);
     const int64_t mt0 = bm * XSTRIPS, nt0 = bn * (2 * FN);
     const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
     const int KT = (int)p.KT;
