@@ -14,6 +14,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -46,9 +47,16 @@ __device__ __forceinline__ float to_f32(uint32_t bits16) {
 // |x| as an integer that orders like |x| (non-NaN), for an exact amax.
 __device__ __forceinline__ uint32_t mag16(uint32_t bits16) { return bits16 & 0x7FFFu; }
 
+// fp32 -> bf16, nearest with ties to even, on gfx950's v_cvt_pk_bf16_f32
+// (one instruction per pair; it equals the bit-level rounding
+// (u + 0x7FFF + lsb) >> 16 on every non-NaN fp32 pattern, and keeps NaNs
+// NaN, which that formula does not for every payload).
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf16));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // nearest, ties to even
+    return f32x2_to_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {

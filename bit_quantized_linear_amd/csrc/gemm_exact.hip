@@ -93,14 +93,18 @@ __device__ __forceinline__ void store_rows_t(const LinParams& p, const float* ba
             for (int t = 0; t < 4; ++t) y[e + t] = c[t] * x[t];
         }
         uint32_t w[4] = {0, 0, 0, 0};
+        if constexpr (OUT == OUT_BF16) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            uint32_t b;
-            if constexpr (OUT == OUT_F32) b = __float_as_uint(y[e]);
-            else if constexpr (OUT == OUT_F16) b = f32_to_f16_bits(y[e]);
-            else if constexpr (OUT == OUT_BF16) b = f32_to_bf16_bits(y[e]);
-            else b = e4m3_encode(y[e] / os);
-            w[e * ESZ / 4] |= b << (8 * ((e * ESZ) % 4));
+            for (int e = 0; e < PER; e += 2) w[e / 2] = f32x2_to_bf16x2(y[e], y[e + 1]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                uint32_t b;
+                if constexpr (OUT == OUT_F32) b = __float_as_uint(y[e]);
+                else if constexpr (OUT == OUT_F16) b = f32_to_f16_bits(y[e]);
+                else b = e4m3_encode(y[e] / os);
+                w[e * ESZ / 4] |= b << (8 * ((e * ESZ) % 4));
+            }
         }
         if (m < p.M && n < p.N)
             *(u4*)((uint8_t*)p.ep.y + (m * p.ep.ldy + n) * ESZ) = u4{w[0], w[1], w[2], w[3]};
