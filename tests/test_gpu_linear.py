@@ -90,7 +90,8 @@ def test_cfg3_llama3_8b(idx, M):
 def test_small_m_two_strip_blocks_odd_count(M):
     """N = 16400: 1025 channel strips, above the count where the small-M fp8
     kernel gives each block two strips, so the last block has one; dynamic
-    quantization (fused for M <= 4), then pre-quantized A (row-major)."""
+    quantization (fused into the GEMV for M <= 4 and, at this short K,
+    M = 16), then pre-quantized A (row-major)."""
     _fp8_case(3, 7, M, 16400, 256, "bf16", False, "channels", torch.bfloat16)
     g = np.random.Generator(np.random.PCG64(54 + M))
     N, K = 16400, 256

@@ -37,9 +37,11 @@ def _act(M, K, dtype, seed):
     return wl.activation(wl.rng(97, seed, M, K), M, K, dtype, "channels")
 
 
-# fused small-M (M <= 4), small-M (M = 16), tiled (M = 128, 1024)
-EQUIV = [(1, 4096, 4096), (4, 6144, 4096), (16, 4096, 14336), (128, 4096, 4096),
-         (1024, 6144, 4096), (3, 1024, 1024), (77, 1040, 528)]
+# fused small-M (M <= 4, and M = 16 at K = 1024), small-M with A quantized
+# by its own launch (M = 16, K = 4096 and 14336), tiled (M = 77, 128, 1024)
+EQUIV = [(1, 4096, 4096), (4, 6144, 4096), (16, 1024, 1024), (16, 6144, 4096),
+         (16, 4096, 14336), (128, 4096, 4096), (1024, 6144, 4096), (3, 1024, 1024),
+         (77, 1040, 528)]
 
 
 @pytest.mark.parametrize("M,N,K", EQUIV)
