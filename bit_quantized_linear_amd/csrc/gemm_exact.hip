@@ -46,16 +46,27 @@ constexpr int XB = 256;                    // block tile edge (rows and columns)
 constexpr int XW = 4;                      // waves per block (2 x 2)
 constexpr int XF = 8;                      // 16-row A strips per wave (128 rows)
 constexpr int XSTRIPS = XB / 16;           // 16-row strips per operand per block
-constexpr int XSTAGE = 2 * XSTRIPS * 1024; // A and B halves of one k-tile: 32 KiB
 constexpr int XS = 4;                      // LDS ring depth (stages)
-constexpr int XLDS = XS * XSTAGE;          // 128 KiB
-constexpr int XLD = 2 * XSTRIPS / XW;      // DMA instructions per wave per stage (8)
 constexpr int XEPI_ROW = XF * 16 * 4 + 16; // epilogue row: up to 128 fp32 values, padded
 constexpr int XEPI_WAVE = XF / 2 * 16 * XEPI_ROW;           // 64 staged rows per wave
 constexpr int XEPI_SCALES = XW * XEPI_WAVE;                 // then 128 column scales per wave
 constexpr int XLDS_EPI = XEPI_SCALES + XW * XF * 16 * 4;
-constexpr int XLDS_ALL = XLDS > XLDS_EPI ? XLDS : XLDS_EPI;
-static_assert(XLD * 2 < 64, "vmcnt range");
+
+// Stage geometry of a block with FN 16-column B strips per wave (2 FN per
+// block).  A stage holds the block's 16 A strips and its B strips rounded up
+// to whole DMA rounds (one slot per wave per round); slots past the block's
+// B strips are loaded out of range (zeros, no memory access) and never read.
+template <int FN>
+struct XCfg {
+    static constexpr int BSLOTS = (2 * FN + XW - 1) / XW * XW;
+    static constexpr int SLOTS = XSTRIPS + BSLOTS;
+    static constexpr int STAGE = SLOTS * 1024;            // half a k-tile of every slot
+    static constexpr int LD = SLOTS / XW;                 // DMA instructions per wave per stage
+    static constexpr int LDS = XS * STAGE;
+    static constexpr int LDS_ALL = LDS > XLDS_EPI ? LDS : XLDS_EPI;
+    static_assert(LD * 2 < 64 && LD <= XF, "vmcnt range; one DMA instruction per step");
+    static_assert(LDS <= XEPI_SCALES, "the column scales lie past the ring");
+};
 
 // Eight E4M3 codes -> eight fp16 of the same values (4 conversions).
 __device__ __forceinline__ v8h dec8(uint32_t d0, uint32_t d1) { return e4m3x8_to_f16(d0, d1); }
@@ -71,10 +82,12 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // unrolled so that their LDS reads overlap.  N is a multiple of 16, so a
 // store's columns lie all inside or all outside N.  Roundings as the other
 // kernels' epilogue: nearest even to fp16 / bf16, E4M3 of fp32(Y / output_scale).
-template <int OUT, int FN>
-__device__ __forceinline__ void store_rows_t(const LinParams& p, const float* band,
+// RAW: the unscaled fp32 sums, into a split-K partial buffer.
+template <int OUT, int FN, bool RAW = false>
+__device__ __forceinline__ void store_rows_t(const LinParams& p, void* dst, int64_t ld, const float* band,
                                              const float* colsc, int64_t rbase, int64_t col0,
                                              int lane) {
+    static_assert(!RAW || OUT == OUT_F32, "partials are fp32");
     constexpr int ESZ = OUT == OUT_E4M3 ? 1 : (OUT == OUT_F32 ? 4 : 2);
     constexpr int PER = 16 / ESZ, CHUNKS = FN * 16 / PER, ITERS = XF / 2 * 16 * CHUNKS / 64;
     static_assert(XF / 2 * 16 * CHUNKS % 64 == 0, "whole stores per lane");
@@ -90,7 +103,7 @@ __device__ __forceinline__ void store_rows_t(const LinParams& p, const float* ba
         for (int e = 0; e < PER; e += 4) {
             const v4f x = *(const v4f*)(src + e), c = *(const v4f*)(colsc + c0 + e);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) y[e + t] = c[t] * x[t];
+            for (int t = 0; t < 4; ++t) y[e + t] = RAW ? x[t] : c[t] * x[t];
         }
         uint32_t w[4] = {0, 0, 0, 0};
         if constexpr (OUT == OUT_BF16) {
@@ -106,8 +119,7 @@ __device__ __forceinline__ void store_rows_t(const LinParams& p, const float* ba
                 w[e * ESZ / 4] |= b << (8 * ((e * ESZ) % 4));
             }
         }
-        if (m < p.M && n < p.N)
-            *(u4*)((uint8_t*)p.ep.y + (m * p.ep.ldy + n) * ESZ) = u4{w[0], w[1], w[2], w[3]};
+        if (m < p.M && n < p.N) *(u4*)((uint8_t*)dst + (m * ld + n) * ESZ) = u4{w[0], w[1], w[2], w[3]};
     }
 }
 
@@ -134,12 +146,14 @@ __device__ __forceinline__ void interleave() {
 
 }  // namespace
 
-// FN: 16-column B strips per wave (8: 256 x 256 blocks; 7: 256 x 224, whose
-// stages still carry 16 B slots, the last two loaded out of range as zeros
-// and never read, so that every wave moves the same 8 KiB per stage).
+// FN: 16-column B strips per wave (8: 256 x 256 blocks, 7: 256 x 224, ...,
+// 4: 256 x 128).  With p.splits > 1, block column blockIdx.y takes k-tiles
+// [blockIdx.y * kt_per_split, + kt_per_split) and writes its raw fp32 sums
+// to that split's partial buffer; the split-K reduce applies the epilogue.
 template <int FN>
 __global__ __launch_bounds__(64 * XW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_exact_kernel(LinParams p) {
+    using C = XCfg<FN>;
     constexpr int BN = 32 * FN;  // block columns
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // the wave index and the tile coordinates (whose 64-bit divisions run on
@@ -153,7 +167,10 @@ void gemm_exact_kernel(LinParams p) {
     bn = __builtin_amdgcn_readfirstlane((int)bn);
     const int64_t mt0 = bm * XSTRIPS, nt0 = bn * (2 * FN);
     const int64_t mtiles = (p.M + 15) / 16, ntiles = p.N / 16;
-    const int KT = (int)p.KT;
+    const int KT = (int)p.KT;  // the operands' k-tile stride
+    // this block's k-tiles: [kt0, kt0 + KTL)
+    const int kt0 = (int)blockIdx.y * (int)p.kt_per_split;
+    const int KTL = KT - kt0 < (int)p.kt_per_split ? KT - kt0 : (int)p.kt_per_split;
 
     // Buffer descriptors over this block's strips: rows past M and channels
     // past N lie beyond them and read as zero.
@@ -165,20 +182,20 @@ void gemm_exact_kernel(LinParams p) {
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.w + nt0 * p.KT * 2048), (short)0, (int)(b_strips * p.KT * 2048), 0x00020000);
 
-    // Half-step s = k-tile s/2, half s%2, goes to ring slot s % XS.  Slot q
-    // of a stage holds A strip q (q < 16) or B strip q - 16; wave w moves
-    // slots w + 4 i, i = 0..7: four A strips, then four B strips.  The first
+    // Half-step s = k-tile kt0 + s/2, half s%2, goes to ring slot s % XS.
+    // Slot q of a stage holds A strip q (q < 16) or B strip q - 16; wave w
+    // moves slots w + 4 i, i < LD: four A strips, then its B strips.  The first
     // stages are issued whole (issue), the later ones one instruction per
     // step of the main loop (issue_one), also past the last stage: those get
     // an out-of-range offset (zeros, no memory access) into a slot nothing
     // reads any more, so that every half-step issues the same loads.
     auto issue = [&](int s) __attribute__((always_inline)) {
-        const int kt = s >> 1, h = s & 1;
-        uint8_t* base = lds + (s % XS) * XSTAGE;
+        const int kt = kt0 + (s >> 1), h = s & 1;
+        uint8_t* base = lds + (s % XS) * C::STAGE;
 #pragma unroll
-        for (int i = 0; i < XLD; ++i) {
+        for (int i = 0; i < C::LD; ++i) {
             const int slot = wave + XW * i;
-            if (i < XLD / 2) {
+            if (i < XSTRIPS / XW) {  // A slots
                 const int off = (slot * KT + kt) * 2048 + h * 1024 + lane * 16;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + slot * 1024), 16, off,
                                                          0, 0, 0);
@@ -189,25 +206,27 @@ void gemm_exact_kernel(LinParams p) {
             }
         }
     };
-    const int H = 2 * KT;
+    const int H = 2 * KTL;
     const int lane16 = lane * 16;
     auto issue_one = [&](int s, int i) __attribute__((always_inline)) {
-        const int kt = s >> 1, h = s & 1, slot = wave + XW * i;
-        uint8_t* dst = lds + (s % XS) * XSTAGE + slot * 1024;
+        if (i >= C::LD) return;
+        const int kt = kt0 + (s >> 1), h = s & 1, slot = wave + XW * i;
+        uint8_t* dst = lds + (s % XS) * C::STAGE + slot * 1024;
         // uniform part of the offset; past the last stage it lies beyond
         // every descriptor's range (at most 2^30 bytes), so all lanes read 0
-        const int strip = i < XLD / 2 ? slot : slot - XSTRIPS;
+        constexpr int A_LD = XSTRIPS / XW;  // the first A_LD instructions move A slots
+        const bool is_a = i < A_LD;
+        const int strip = is_a ? slot : slot - XSTRIPS;
         const int uoff = s < H ? (strip * KT + kt) * 2048 + h * 1024 : 0x7FFF0000;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < XLD / 2 ? ra : rb, (lds_ptr_t)dst, 16, lane16 + uoff, 0,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (lds_ptr_t)dst, 16, lane16 + uoff, 0, 0, 0);
     };
     // A lane's 16 bytes of strip i of this wave (A) / j (B) in half-step s:
     // bytes 0-7 feed MFMA slice 0, bytes 8-15 slice 1 (same k map for both).
     auto read_a = [&](int s, int i) __attribute__((always_inline)) {
-        return *(const u4*)(lds + (s % XS) * XSTAGE + (wm * XF + i) * 1024 + lane * 16);
+        return *(const u4*)(lds + (s % XS) * C::STAGE + (wm * XF + i) * 1024 + lane * 16);
     };
     auto read_b = [&](int s, int j) __attribute__((always_inline)) {
-        return *(const u4*)(lds + (s % XS) * XSTAGE + (XSTRIPS + wn * FN + j) * 1024 + lane * 16);
+        return *(const u4*)(lds + (s % XS) * C::STAGE + (XSTRIPS + wn * FN + j) * 1024 + lane * 16);
     };
 
     const int64_t m0 = bm * XB + wm * XF * 16, col0 = bn * BN + wn * FN * 16;
@@ -232,8 +251,8 @@ void gemm_exact_kernel(LinParams p) {
     for (int s = 0; s < XS - 1; ++s)
         if (s < H) issue(s);
     // stage 0 is in (stages issued after it: min(H - 1, 2)); H >= 2
-    if (H >= 3) wait_vmcnt<2 * XLD>();
-    else if (H == 2) wait_vmcnt<XLD>();
+    if (H >= 3) wait_vmcnt<2 * C::LD>();
+    else if (H == 2) wait_vmcnt<C::LD>();
     else wait_vmcnt<0>();
     compiler_fence();
     lds_barrier();
@@ -259,7 +278,7 @@ void gemm_exact_kernel(LinParams p) {
         // that every wave has consumed the slot that stage s+3 overwrites
         // (its reads completed in half-step s-1, when their data was
         // decoded), so it needs no wait on LDS reads
-        if (s + 2 < H) wait_vmcnt<XLD>();
+        if (s + 2 < H) wait_vmcnt<C::LD>();
         else wait_vmcnt<0>();
         compiler_fence();
         __builtin_amdgcn_s_barrier();
@@ -319,26 +338,36 @@ void gemm_exact_kernel(LinParams p) {
                         acc[IB + i][j][r];
     };
     // the staged rows and scales are written and read back by this wave only
-    auto epilogue = [&](auto out_tag) __attribute__((always_inline)) {
+    auto epilogue = [&](auto out_tag, auto raw_tag, void* dst, int64_t ld) __attribute__((always_inline)) {
         constexpr int OUT = decltype(out_tag)::value;
+        constexpr bool RAW = decltype(raw_tag)::value;
         stage(std::integral_constant<int, 0>{});
         __builtin_amdgcn_wave_barrier();
-        store_rows_t<OUT, FN>(p, band, colsc, m0, col0, lane);
+        store_rows_t<OUT, FN, RAW>(p, dst, ld, band, colsc, m0, col0, lane);
         __builtin_amdgcn_wave_barrier();
         stage(std::integral_constant<int, XF / 2>{});
         __builtin_amdgcn_wave_barrier();
-        store_rows_t<OUT, FN>(p, band, colsc, m0 + XF / 2 * 16, col0, lane);
+        store_rows_t<OUT, FN, RAW>(p, dst, ld, band, colsc, m0 + XF / 2 * 16, col0, lane);
     };
+    if (p.splits > 1) {
+        float* part = (float*)p.partial + (int64_t)blockIdx.y * p.M * p.N;
+        epilogue(std::integral_constant<int, OUT_F32>{}, std::true_type{}, part, p.N);
+        return;
+    }
+    const std::false_type scaled;
+    void* y = p.ep.y;
+    const int64_t ldy = p.ep.ldy;
     switch (p.ep.ydt) {
-        case OUT_BF16: epilogue(std::integral_constant<int, OUT_BF16>{}); break;
-        case OUT_F16: epilogue(std::integral_constant<int, OUT_F16>{}); break;
-        case OUT_F32: epilogue(std::integral_constant<int, OUT_F32>{}); break;
-        default: epilogue(std::integral_constant<int, OUT_E4M3>{}); break;
+        case OUT_BF16: epilogue(std::integral_constant<int, OUT_BF16>{}, scaled, y, ldy); break;
+        case OUT_F16: epilogue(std::integral_constant<int, OUT_F16>{}, scaled, y, ldy); break;
+        case OUT_F32: epilogue(std::integral_constant<int, OUT_F32>{}, scaled, y, ldy); break;
+        default: epilogue(std::integral_constant<int, OUT_E4M3>{}, scaled, y, ldy); break;
     }
 }
 
 template <int FN>
 static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
+    using C = XCfg<FN>;
     // dynamic LDS above 64 KiB needs the attribute, set once per device
     // (before any graph capture: the first launch is eager)
     static std::atomic<uint64_t> configured{0};
@@ -348,25 +377,62 @@ static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
     const uint64_t bit = uint64_t(1) << (dev & 63);
     if (!(configured.load(std::memory_order_acquire) & bit)) {
         e = hipFuncSetAttribute((const void*)gemm_exact_kernel<FN>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_ALL);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_ALL);
         if (e != hipSuccess) return e;
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
     const int64_t blocks = ((p.M + XB - 1) / XB) * ((p.N + 32 * FN - 1) / (32 * FN));
-    gemm_exact_kernel<FN><<<(unsigned)blocks, 64 * XW, XLDS_ALL, stream>>>(p);
+    gemm_exact_kernel<FN><<<dim3((unsigned)blocks, (unsigned)p.splits), 64 * XW, C::LDS_ALL, stream>>>(p);
     return hipGetLastError();
 }
 
-// One block per CU at a time: the busiest CU runs ceil(tiles / CUs) tiles,
-// so 224-column tiles win where they even the rounds out (M = 1024,
-// N = 28672: 448 tiles of 256 take two rounds, 512 of 224 two rounds of
-// 7/8 the work).
-hipError_t launch_gemm_exact(const LinParams& p, hipStream_t stream) {
+// Block width (fn strips of 16 columns per wave) and K splits for a shape,
+// from a cost model in microseconds fitted to timings of every (fn, splits)
+// at M = 256 .. 4096 on Llama-shaped N x K (MI355X).  One block per CU at a
+// time, so a launch takes full rounds of CUS blocks and a tail round (whose
+// k-tiles run a little faster: fewer busy CUs, higher clock); a k-tile of a
+// block costs a fixed part (the A side: its 16 strips' DMA, reads and
+// conversions) and a part per B strip; K splits add the fp32 partials'
+// write and read and the reduce launch.  Below M = 513 the 128-row kernels
+// measured as fast or faster.
+ExactPlan exact_plan(int64_t M, int64_t N, int64_t K) {
     constexpr int64_t CUS = 256;
-    const int64_t mt = (p.M + XB - 1) / XB;
-    const int64_t t8 = mt * ((p.N + 255) / 256), t7 = mt * ((p.N + 223) / 224);
-    if (((t7 + CUS - 1) / CUS) * 224 < ((t8 + CUS - 1) / CUS) * 256) return launch_fn<7>(p, stream);
-    return launch_fn<8>(p, stream);
+    constexpr double KTILE_US = 0.76, KTILE_US_PER_FN = 0.25, BLOCK_US = 1.3, TAIL_SPEED = 0.95;
+    constexpr double PARTIAL_BYTES_PER_US = 5.0e6, REDUCE_US = 10.0;
+    constexpr int FNS[] = {8, 7, 6, 4, 3, 2};
+    ExactPlan best{0, 1};
+    if (M <= 512) return best;
+    const int64_t KT = (K + 127) / 128, mt = (M + XB - 1) / XB;
+    double best_us = 0;
+    for (int fn : FNS) {
+        const int64_t tiles = mt * ((N + 32 * fn - 1) / (32 * fn));
+        const double ktile = KTILE_US + KTILE_US_PER_FN * fn;
+        for (int s = 1; s <= 4; ++s) {
+            const int64_t per = (KT + s - 1) / s, splits = (KT + per - 1) / per;
+            if (splits != s || (s > 1 && per < 4)) continue;
+            const int64_t full = tiles * s / CUS, tail = tiles * s % CUS;
+            double us = full * (BLOCK_US + per * ktile);
+            if (tail) us += BLOCK_US + per * ktile * (TAIL_SPEED + (1 - TAIL_SPEED) * tail / CUS);
+            if (s > 1) us += (double)s * M * N * 8 / PARTIAL_BYTES_PER_US + REDUCE_US;
+            if (best.fn == 0 || us < best_us) {
+                best = ExactPlan{fn, s};
+                best_us = us;
+            }
+        }
+    }
+    return best;
+}
+
+hipError_t launch_gemm_exact(const LinParams& p, int fn, hipStream_t stream) {
+    switch (fn) {
+        case 8: return launch_fn<8>(p, stream);
+        case 7: return launch_fn<7>(p, stream);
+        case 6: return launch_fn<6>(p, stream);
+        case 4: return launch_fn<4>(p, stream);
+        case 3: return launch_fn<3>(p, stream);
+        case 2: return launch_fn<2>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace bql

@@ -1180,12 +1180,11 @@ static hipError_t launch_gemm_ks(const LinParams& p, hipStream_t stream) {
 // k-split exact kernel and the register-prefetching fp8 kernel with a
 // three-stage ring; shapes with many 256x256 tiles favour the big fp8 tile.
 constexpr int64_t CUS = 256;
-// Exact fp8 shapes with at least this many 256x256 output tiles run the
-// 256x256 kernel of gemm_exact.hip.
-constexpr int64_t EXACT_BIG_TILES = 384;
-// Exact fp8 with at most one 128x128 output tile per CU runs the k-split kernel.
-static bool uses_ks(int variant, int64_t M, int64_t N) {
-    return variant == V_FP8X && ((M + 127) / 128) * ((N + 127) / 128) <= CUS;
+// Exact fp8 runs the 256-row kernel of gemm_exact.hip where exact_plan
+// takes the shape (M >= 256); below that, with at most one 128x128 output
+// tile per CU, the k-split kernel.
+static bool uses_ks(int variant, int64_t M, int64_t N, int64_t K) {
+    return variant == V_FP8X && exact_plan(M, N, K).fn == 0 && ((M + 127) / 128) * ((N + 127) / 128) <= CUS;
 }
 
 // Row-major 8-bit A (per-lane gathers of 16-byte chunks from 16 rows)
@@ -1193,7 +1192,7 @@ static bool uses_ks(int variant, int64_t M, int64_t N) {
 // than a repack launch: at M = 1024, +3 % for the exact 128x128 kernel at
 // N = 28672 and +37 % for W4A8, against -5 to -9 % for the k-split kernel.
 bool reads_rowmajor_a(int variant, int64_t M, int64_t N, int64_t K) {
-    return use_small_m(variant, M, N, K) || uses_ks(variant, M, N);
+    return use_small_m(variant, M, N, K) || uses_ks(variant, M, N, K);
 }
 
 // K splits of the 128 x 128 tile kernels that take them (the exact k-split
@@ -1205,16 +1204,17 @@ bool reads_rowmajor_a(int variant, int64_t M, int64_t N, int64_t K) {
 // ceil(KT / s) k-tiles, plus the partials' write and read (8 bytes per
 // output and split; a 128 x 128 block's k-tile takes about as long as the
 // chip moves 4 MB).  At most 8 splits of 4+ k-tiles.
-static bool tile_splittable(int variant, int64_t M, int64_t N) {
+static bool tile_splittable(int variant, int64_t M, int64_t N, int64_t K) {
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (variant == V_FP8X) return t256 < EXACT_BIG_TILES && uses_ks(variant, M, N);
+    if (variant == V_FP8X) return uses_ks(variant, M, N, K);
     if (variant == V_FP8) return t128 <= CUS;
     return variant == V_W4A8 || variant == V_W4A8G;
 }
 
 static int tile_splits(int variant, int64_t M, int64_t N, int64_t K) {
-    if (use_small_m(variant, M, N, K) || !tile_splittable(variant, M, N)) return 1;
+    if (use_small_m(variant, M, N, K)) return 1;
+    if (variant == V_FP8X && exact_plan(M, N, K).fn != 0) return exact_plan(M, N, K).splits;
+    if (!tile_splittable(variant, M, N, K)) return 1;
     constexpr double BYTES_PER_KTILE = 4e6;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128), kt = (K + TILE_K - 1) / TILE_K;
     int best = 1;
@@ -1263,12 +1263,13 @@ static hipError_t run_gemm_kernel(const LinParams& p, hipStream_t stream) {
     const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
     if constexpr (V == V_FP8X) {
-        // many 256x256 tiles: the 128x128-per-wave kernel (half the
-        // conversions per MFMA of the 64x64-per-wave kernels)
-        if (t256 >= EXACT_BIG_TILES) return launch_gemm_exact(p, stream);
+        // M >= 256: the 128-row-per-wave kernel (half the conversions per
+        // MFMA of the 64x64-per-wave kernels), with its K splits
+        const ExactPlan xp = exact_plan(p.M, p.N, p.K);
+        if (xp.fn != 0) return launch_gemm_exact(p, xp.fn, stream);
         // at most one 128x128 tile per CU: a four-stage ring, so that each
         // k-tile's DMA has three k-tiles of compute to land behind
-        if (uses_ks(V, p.M, p.N)) return launch_gemm_ks<128, 128, 2, 2, 4>(p, stream);
+        if (uses_ks(V, p.M, p.N, p.K)) return launch_gemm_ks<128, 128, 2, 2, 4>(p, stream);
         // Two blocks share a CU, so the busiest CU carries ceil(tiles / CUs)
         // tiles: 128x96 tiles win where they even that out (M = 1024, N =
         // 6144: 384 tiles of 128 columns leave half the CUs with two, 512

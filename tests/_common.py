@@ -114,3 +114,34 @@ class Weights:
             self.codes, s = oracle.quant_per_tensor(wf)
             self.scales = np.array([s], dtype=np.float32)
         del wf
+
+
+def exact_plan(M: int, N: int, K: int) -> tuple:
+    """(fn, splits) of the exact fp8 tile kernel for an M x N x K linear:
+    blocks of 256 rows x 32 fn columns (each wave 128 rows x fn 16-column
+    strips), K split `splits` ways; (0, 1) where the 128-row kernels run
+    (M <= 512).  The library's cost model in microseconds: rounds of 256
+    blocks (one per CU), a tail round a little faster, a k-tile costing
+    0.76 + 0.25 fn, 1.3 per block, and for K splits the fp32 partials at
+    5 MB/us plus 10 for the reduce.  test_abi_host checks the split counts
+    against the library's workspace sizes."""
+    best, best_us = (0, 1), None
+    if M <= 512:
+        return best
+    KT, mt = (K + 127) // 128, (M + 255) // 256
+    for fn in (8, 7, 6, 4, 3, 2):
+        tiles = mt * ((N + 32 * fn - 1) // (32 * fn))
+        ktile = 0.76 + 0.25 * fn
+        for s in range(1, 5):
+            per = (KT + s - 1) // s
+            if (KT + per - 1) // per != s or (s > 1 and per < 4):
+                continue
+            full, tail = divmod(tiles * s, 256)
+            us = full * (1.3 + per * ktile)
+            if tail:
+                us += 1.3 + per * ktile * (0.95 + 0.05 * tail / 256)
+            if s > 1:
+                us += s * M * N * 8 / 5.0e6 + 10.0
+            if best_us is None or us < best_us:
+                best, best_us = (fn, s), us
+    return best

@@ -282,3 +282,27 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         bql.quantize_dynamic(torch.zeros(16, dtype=torch.float16))
+
+
+def test_exact_tile_plan_mirror(L):
+    """The test-side mirror of the exact fp8 kernel's planner gives the split
+    count the library sizes its workspace for (shapes where the fast fp8
+    kernels do not split, so the fp8 workspace holds the exact path's
+    partials only)."""
+    from _common import exact_plan
+    checked = 0
+    for M in (513, 520, 777, 1000, 1024, 1300, 2048, 4096):
+        for N in (1040, 2096, 4096, 6144, 8192, 10240, 16352, 28672, 57344):
+            for K in (1000, 2000, 4000, 4096, 8192, 14336, 28672):
+                if ((M + 127) // 128) * ((N + 127) // 128) <= 256:
+                    continue
+                ws = L.bql_fp8_linear_workspace_size(M, N, K)
+                aq = ((M + 15) // 16) * ((K + 127) // 128) * 2048
+                extra = ws - 8192 - (aq + 255) // 256 * 256
+                fn, s = exact_plan(M, N, K)
+                assert fn != 0
+                want = (M * N * 4 * s + 255) // 256 * 256 if s > 1 else 0
+                assert extra == want, (M, N, K, fn, s, extra)
+                checked += 1
+    assert checked > 300
+

@@ -1,10 +1,11 @@
-"""GPU parity of the exact fp8 tile kernel for large M (256 x 256 blocks, one
-128 x 128 output tile per wave), against the CPU oracle.
+"""GPU parity of the exact fp8 tile kernel for M > 512 (blocks of 256 rows
+by 32 fn columns, each wave 128 rows by fn 16-column strips, K split over
+blocks where the planner says so), against the CPU oracle.
 
 The fp8 linear Y = (sA sW[n]) (Aq Wq^T) of vLLM PR #4118 with dynamic
-per-tensor activation scaling, exact products summed in fp32.  These shapes
-have enough 256 x 256 output tiles that bql_fp8_linear runs this kernel:
-the Llama-3-8B MLP up-projection at M = 1024, ragged M / N / K (partial
+per-tensor activation scaling, exact products summed in fp32.  Covered:
+every block width the planner uses (fn = 2, 3, 4, 6, 7, 8) with 1 to 4 K
+splits, the Llama-3-8B projections at M = 1024, ragged M / N / K (partial
 row and column tiles, K padded inside the operand tiles), fp32 and fp8
 outputs (vLLM discussion #5802, output_scale), per-channel weight scales
 (optimum-quanto PR #241) and pre-quantized E4M3 activations.  Float
@@ -17,8 +18,8 @@ import torch
 
 import oracle
 import workloads as wl
-from _common import (DEV, Weights, assert_close, assert_fp8_out, dev16, host, host_f64, rows_for,
-                     say)
+from _common import (DEV, Weights, assert_close, assert_fp8_out, dev16, exact_plan, host, host_f64,
+                     rows_for, say)
 
 import bit_quantized_linear_amd as bql
 
@@ -26,9 +27,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(M, N, K, idx, per_channel=False, out_dtype=torch.bfloat16, prequant=False, fp8_out=False):
-    say(f"exact tile: M={M} N={N} K={K} per_channel={per_channel} out={out_dtype} "
-        f"prequant={prequant} fp8_out={fp8_out}")
-    assert ((M + 255) // 256) * ((N + 255) // 256) >= 384, "shape must select the 256x256 kernel"
+    say(f"exact tile: M={M} N={N} K={K} plan={exact_plan(M, N, K)} per_channel={per_channel} "
+        f"out={out_dtype} prequant={prequant} fp8_out={fp8_out}")
+    assert exact_plan(M, N, K)[0] != 0, "shape must select the exact tile kernel"
     W = Weights(97, idx, N, K, "bf16", per_channel)
     pw = bql.prepack_weight(dev16(W.bits, "bf16"), "fp8_channel" if per_channel else "fp8_tensor")
     assert np.array_equal(host(pw.scales).view(np.uint32), W.scales.view(np.uint32))
@@ -77,13 +78,37 @@ def test_prequantized_e4m3_activations():
     _run(1024, 28672, 4096, 4, prequant=True)
 
 
+# (M, N, K) -> (fn, splits): each block width and split count the planner
+# uses, with partial row tiles (M % 256 != 0), partial column blocks and K
+# not a multiple of 128
+PLANS = [((520, 1040, 1008), (2, 1)), ((520, 1040, 2000), (2, 4)), ((520, 5792, 1008), (3, 1)),
+         ((1000, 1568, 4000), (3, 3)), ((520, 8432, 1008), (4, 1)), ((777, 2096, 4000), (4, 3)),
+         ((520, 11072, 1008), (6, 1)), ((520, 7376, 8000), (6, 2)), ((520, 16352, 1008), (7, 1)),
+         ((520, 4208, 8000), (7, 4)), ((520, 19520, 1008), (8, 1)), ((520, 9488, 14336), (8, 2))]
+
+
+@pytest.mark.parametrize("shape,plan", PLANS)
+def test_every_block_width_and_split(shape, plan):
+    # split shapes also check the fp8 output (the reduce's epilogue); every
+    # other shape takes per-channel weight scales
+    i = PLANS.index((shape, plan))
+    assert exact_plan(*shape) == plan
+    _run(*shape, 10 + i, per_channel=i % 2 == 1, fp8_out=plan[1] > 1)
+
+
+# the Llama-3-8B projections of the fp8 step at M = 1024
+@pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 4096), (4096, 14336)])
+def test_llama3_projections_m1024(N, K):
+    _run(1024, N, K, 30 + N + K)
+
+
 def test_single_k_tile():
     # K = 128: two half-steps only (the shortest pipeline)
-    _run(512, 49152, 128, 5)
+    _run(520, 49152, 128, 5)
 
 
-def test_deterministic():
-    M, N, K = 512, 49152, 512
+@pytest.mark.parametrize("M,N,K", [(640, 49152, 512), (777, 2096, 4000)])
+def test_deterministic(M, N, K):
     W = Weights(97, 6, N, K, "bf16", False)
     pw = bql.prepack_weight(dev16(W.bits, "bf16"), "fp8_tensor")
     a = dev16(wl.activation(wl.rng(97, 6, M, 3), M, K, "bf16", "channels"), "bf16")
