@@ -398,7 +398,7 @@ static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
 ExactPlan exact_plan(int64_t M, int64_t N, int64_t K) {
     constexpr int64_t CUS = 256;
     constexpr double KTILE_US = 0.76, KTILE_US_PER_FN = 0.25, BLOCK_US = 1.3, TAIL_SPEED = 0.95;
-    constexpr double PARTIAL_BYTES_PER_US = 5.0e6, REDUCE_US = 10.0;
+    constexpr double PARTIAL_BYTES_PER_US = 6.0e6, REDUCE_US = 6.0;
     constexpr int FNS[] = {8, 7, 6, 4, 3, 2};
     ExactPlan best{0, 1};
     if (M <= 512) return best;

@@ -344,17 +344,36 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
     }
 }
 
-// Fixed-order sum of the split-K partials, then the epilogue.
+// Fixed-order sum of the split-K partials, then the epilogue: four
+// consecutive outputs of a row per thread (N is a multiple of 16), read
+// with 16-byte loads from each split and written with one store.
 template <int V>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(LinParams p) {
     using E = typename VT<V>::E;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= p.M * p.N) return;
+    using E4 = E __attribute__((ext_vector_type(4)));
+    const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4, total = p.M * p.N;
+    if (idx >= total) return;
     const E* part = (const E*)p.partial;
-    E s = part[idx];
-    for (int k = 1; k < p.splits; ++k) s += part[(int64_t)k * p.M * p.N + idx];
+    E4 s = *(const E4*)(part + idx);
+    for (int k = 1; k < p.splits; ++k) s += *(const E4*)(part + k * total + idx);
     const float sa = (V == V_FP8 || V == V_FP8X) ? *p.ep.a_scale : 1.0f;
-    finish<V>(p, sa, idx / p.N, idx % p.N, s);
+    const int64_t m = idx / p.N, n = idx % p.N;
+    uint32_t b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b[t] = out_bits<V>(p.ep, sa, m, n + t, s[t]);
+    uint8_t* y = (uint8_t*)p.ep.y;
+    const int esz = out_size(p.ep.ydt);
+    const int64_t at = (m * p.ep.ldy + n) * esz;
+    if (esz == 4) *(u4*)(y + at) = u4{b[0], b[1], b[2], b[3]};
+    else if (esz == 2) *(u2*)(y + at) = u2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+    else *(uint32_t*)(y + at) = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+}
+
+template <int V>
+static hipError_t launch_splitk_reduce(const LinParams& p, hipStream_t stream) {
+    const int64_t quads = p.M * p.N / 4;
+    splitk_reduce_kernel<V><<<(unsigned)((quads + 255) / 256), 256, 0, stream>>>(p);
+    return hipGetLastError();
 }
 
 // --------------------------------------------------------------- large M
@@ -1101,11 +1120,9 @@ static hipError_t run_gemv(LinParams p, hipStream_t stream) {
     }
     dim3 grid((unsigned)strips, (unsigned)p.splits, (unsigned)((p.M + 15) / 16));
     gemv_kernel<V, 1, GEMV_WAVES, GEMV_U, FUSED><<<grid, 64 * GEMV_WAVES, lds, stream>>>(p);
-    if (p.splits > 1) {
-        const int64_t total = p.M * p.N;
-        splitk_reduce_kernel<V><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
-    }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_reduce<V>(p, stream);
 }
 
 template <int V, int BM, int BN, int WM, int WN, int S>
@@ -1253,9 +1270,7 @@ static hipError_t run_gemm(const LinParams& p0, hipStream_t stream) {
     }
     hipError_t e = run_gemm_kernel<V>(p, stream);
     if (e != hipSuccess || p.splits == 1) return e;
-    const int64_t total = p.M * p.N;
-    splitk_reduce_kernel<V><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
-    return hipGetLastError();
+    return launch_splitk_reduce<V>(p, stream);
 }
 
 template <int V>
@@ -1340,9 +1355,7 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
         p.splits = (int)((p.KT + p.kt_per_split - 1) / p.kt_per_split);
         hipError_t e = launch_gemm_w4a16(p, stream);
         if (e != hipSuccess || p.splits == 1) return e;
-        const int64_t total = p.M * p.N;
-        splitk_reduce_kernel<V_W4A16G><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
-        return hipGetLastError();
+        return launch_splitk_reduce<V_W4A16G>(p, stream);
     }
     if (args.a_rowmajor && !reads_rowmajor_a(args.variant, args.M, args.N, args.K))
         return hipErrorInvalidValue;  // this shape's tile kernel takes packed A

@@ -123,7 +123,7 @@ def exact_plan(M: int, N: int, K: int) -> tuple:
     (M <= 512).  The library's cost model in microseconds: rounds of 256
     blocks (one per CU), a tail round a little faster, a k-tile costing
     0.76 + 0.25 fn, 1.3 per block, and for K splits the fp32 partials at
-    5 MB/us plus 10 for the reduce.  test_abi_host checks the split counts
+    6 MB/us plus 6 for the reduce.  test_abi_host checks the split counts
     against the library's workspace sizes."""
     best, best_us = (0, 1), None
     if M <= 512:
@@ -141,7 +141,7 @@ def exact_plan(M: int, N: int, K: int) -> tuple:
             if tail:
                 us += 1.3 + per * ktile * (0.95 + 0.05 * tail / 256)
             if s > 1:
-                us += s * M * N * 8 / 5.0e6 + 10.0
+                us += s * M * N * 8 / 6.0e6 + 6.0
             if best_us is None or us < best_us:
                 best, best_us = (fn, s), us
     return best
