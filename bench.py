@@ -802,6 +802,8 @@ def main():
                     help="output rows the CPU oracle computes per configuration row")
     ap.add_argument("--configs-only", action="store_true",
                     help="only the per-configuration rows")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the M=1024 step (for a rocprofv3 run of its kernels)")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel launches (for a rocprofv3 run of that kernel)")
     ap.add_argument("--rmsnorm-only", action="store_true",
@@ -900,6 +902,10 @@ def main():
         log("timing M=1024 exact ...")
         abits, _, _, _, (sec, sec_eager), flops, byts, a_copies = run_pass(M)
         value = flops / sec / 1e12
+        if args.step_only:
+            print(json.dumps({"value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(sec * 1e3, 4),
+                              "eager_value": round(flops / sec_eager / 1e12, 2)}), flush=True)
+            return
 
     # dominant kernel: the tiled GEMM of the (28672, 4096) linear, pre-quantized A
     def kernel_roofline(fast):
