@@ -10,6 +10,7 @@ calling a compute function without the built library raises.
 Operations (see the header for the exact contracts):
   quantize_dynamic        per-tensor E4M3 with scale = amax / 448
   quantize_static         E4M3 with a given scale
+  pack_activations        E4M3 codes into the tile layout fp8_linear reads (M > 16)
   int8_quantize_per_token per-row int8 with scale = amax / 127
   rmsnorm_int8_quantize_per_token   RMSNorm fused with per-row int8
   rmsnorm_fp8_quantize_dynamic      RMSNorm fused with per-tensor E4M3
@@ -36,7 +37,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbql.so")
 
 # bql_dtype
-F16, BF16, F32, E4M3, I8, I32, INT4 = 1, 2, 3, 4, 5, 6, 7
+F16, BF16, F32, E4M3, I8, I32, INT4, E4M3_TILES = 1, 2, 3, 4, 5, 6, 7, 8
 # bql_wfmt
 WFMT = {"fp8_tensor": 1, "fp8_channel": 2, "int4_channel": 3, "int4_group": 4}
 STATUS = {0: "BQL_OK", 1: "BQL_ERR_NULL", 2: "BQL_ERR_DTYPE", 3: "BQL_ERR_SHAPE",
@@ -64,6 +65,8 @@ SIGNATURES = {
     "bql_quantize_workspace_size": (_SZ, [_I64]),
     "bql_fp8_quantize_dynamic": (_I, [_P, _I, _I64, _P, _P, _P, _SZ, _P]),
     "bql_fp8_quantize_static": (_I, [_P, _I, _I64, _P, _P, _P]),
+    "bql_fp8_packed_activation_bytes": (_SZ, [_I64, _I64]),
+    "bql_fp8_pack_activations": (_I, [_P, _I64, _I64, _P, _P]),
     "bql_int8_quantize_per_token": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bql_rmsnorm_quantize_workspace_size": (_SZ, [_I64]),
     "bql_rmsnorm_int8_quantize_per_token": (_I, [_P, _P, _I, _I64, _I64, ctypes.c_float, _P, _P,
@@ -152,6 +155,28 @@ def quantize_dynamic(x: torch.Tensor, ws: Optional[torch.Tensor] = None):
            L.bql_fp8_quantize_dynamic(_ptr(x), _TORCH_TO_BQL[x.dtype], x.numel(), _ptr(xq),
                                       _ptr(scale), _ptr(ws), nb, _stream(x.device)))
     return xq, scale
+
+
+@dataclass
+class PackedActivations:
+    """E4M3 activation codes [M,K] in the library's operand-tile layout."""
+    packed: torch.Tensor   # uint8, private tile layout
+    M: int
+    K: int
+
+
+def pack_activations(codes: torch.Tensor) -> PackedActivations:
+    """Row-major E4M3 codes [M,K] (uint8 or float8_e4m3fn) into the layout
+    the large-M fp8 GEMMs read, for fp8_linear calls that should not repack
+    A each time (M > 16)."""
+    _need_cuda(codes)
+    L = lib()
+    M, K = codes.shape
+    packed = torch.empty(max(16, L.bql_fp8_packed_activation_bytes(M, K)), dtype=torch.uint8,
+                         device=codes.device)
+    _check("bql_fp8_pack_activations",
+           L.bql_fp8_pack_activations(_ptr(codes), M, K, _ptr(packed), _stream(codes.device)))
+    return PackedActivations(packed, M, K)
 
 
 def quantize_static(x: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
@@ -286,20 +311,25 @@ def fp8_linear(a: torch.Tensor, pw: PackedWeight, a_scale: Optional[torch.Tensor
 
     a fp16/bf16 [M,K]: quantized dynamically per tensor (the scale used is
     written to `a_scale` if given, an fp32 [1] tensor).  a uint8 /
-    float8_e4m3fn codes: pre-quantized, `a_scale` required.
+    float8_e4m3fn codes: pre-quantized, `a_scale` required; a
+    PackedActivations (M > 16): the same codes already packed.
     out_dtype float16 / bfloat16 / float32, or float8_e4m3fn/uint8 with
     `output_scale`.  fast_accum=True uses the fp8 matrix cores' own
     accumulation (BQL_ACCUM_FAST) instead of exact products summed in fp32."""
+    if isinstance(a, PackedActivations):
+        M, K, adt, a = a.M, a.K, E4M3_TILES, a.packed
+    else:
+        M, K = a.shape
+        adt = _TORCH_TO_BQL[a.dtype]
     _need_cuda(a, a_scale, output_scale, out, ws)
     L = lib()
-    M, K = a.shape
     N = pw.N
     ydt = _TORCH_TO_BQL[out_dtype]
     if out is None:
         out = torch.empty((M, N), dtype=torch.uint8 if ydt == E4M3 else out_dtype, device=a.device)
     ws, nb = _workspace(L.bql_fp8_linear_workspace_size(M, N, K), a.device, ws)
     _check("bql_fp8_linear",
-           L.bql_fp8_linear(_ptr(a), _TORCH_TO_BQL[a.dtype], _ptr(a_scale), _ptr(pw.packed),
+           L.bql_fp8_linear(_ptr(a), adt, _ptr(a_scale), _ptr(pw.packed),
                             _ptr(pw.scales), int(pw.per_channel), M, N, K, _ptr(output_scale),
                             _ptr(out), ydt, int(bool(fast_accum)), _ptr(ws), nb, _stream(a.device)))
     return out

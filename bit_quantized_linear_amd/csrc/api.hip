@@ -169,6 +169,22 @@ bql_status bql_fp8_quantize_static(const void* x, bql_dtype xdt, int64_t numel, 
     return hip_status(bql::launch_quant_static(x, xdt, numel, scale, xq, (hipStream_t)stream));
 }
 
+size_t bql_fp8_packed_activation_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    return bql::packed_act_bytes(M, K);
+}
+
+bql_status bql_fp8_pack_activations(const uint8_t* codes, int64_t M, int64_t K, void* packed,
+                                    bql_stream stream) {
+    CHECK(need_m(M));
+    if (K <= 0 || K % 16 || K > (int64_t(1) << 22))
+        return fail(BQL_ERR_SHAPE, "K=%lld must be a positive multiple of 16, at most 2^22", (long long)K);
+    if (M == 0) return ok();
+    CHECK(need_ptr(codes, "codes"));
+    CHECK(need_ptr(packed, "packed"));
+    return hip_status(bql::launch_pack_codes(codes, M, K, (uint8_t*)packed, (hipStream_t)stream));
+}
+
 bql_status bql_int8_quantize_per_token(const void* x, bql_dtype xdt, int64_t M, int64_t K,
                                        int8_t* xq, float* scales, bql_stream stream) {
     if (!is_f16ish(xdt)) return fail(BQL_ERR_DTYPE, "x must be BQL_F16 or BQL_BF16");
@@ -355,7 +371,11 @@ static bql_status check_fp8_linear(const void* a, bql_dtype adt, const float* a_
     CHECK(need_m(M));
     CHECK(need_nk_fp8(N, K));
     if (K > (int64_t(1) << 22)) return fail(BQL_ERR_SHAPE, "K above 2^22");
-    if (!is_f16ish(adt) && adt != BQL_E4M3) return fail(BQL_ERR_DTYPE, "A must be BQL_F16, BQL_BF16 or BQL_E4M3");
+    if (!is_f16ish(adt) && adt != BQL_E4M3 && adt != BQL_E4M3_TILES)
+        return fail(BQL_ERR_DTYPE, "A must be BQL_F16, BQL_BF16, BQL_E4M3 or BQL_E4M3_TILES");
+    if (adt == BQL_E4M3_TILES && M != 0 && (M <= bql::SMALL_M_MAX || N <= bql::SKINNY_MAX_N))
+        return fail(BQL_ERR_SHAPE, "BQL_E4M3_TILES activations need M > %d and N >= 16 (M=%lld N=%lld)",
+                    (int)bql::SMALL_M_MAX, (long long)M, (long long)N);
     if (ydt != BQL_F16 && ydt != BQL_BF16 && ydt != BQL_F32 && ydt != BQL_E4M3)
         return fail(BQL_ERR_DTYPE, "Y must be BQL_F16, BQL_BF16, BQL_F32 or BQL_E4M3");
     if (w_per_channel != 0 && w_per_channel != 1) return fail(BQL_ERR_ARG, "w_per_channel must be 0 or 1");
@@ -365,7 +385,7 @@ static bql_status check_fp8_linear(const void* a, bql_dtype adt, const float* a_
     CHECK(need_ptr(w_packed, "w_packed"));
     CHECK(need_scalar(w_scale, "w_scale"));
     CHECK(need_ptr(y, "y"));
-    if (adt == BQL_E4M3) CHECK(need_scalar(a_scale, "a_scale"));
+    if (adt == BQL_E4M3 || adt == BQL_E4M3_TILES) CHECK(need_scalar(a_scale, "a_scale"));
     else if (a_scale && (((uintptr_t)a_scale) & 3u)) return fail(BQL_ERR_ALIGN, "a_scale misaligned");
     if (ydt == BQL_E4M3) CHECK(need_scalar(output_scale, "output_scale"));
     return BQL_OK;
@@ -384,7 +404,8 @@ static bql_status run_fp8_linear(const void* a, bql_dtype adt, float* a_scale, c
     uint8_t* aq = (uint8_t*)(wsb + bql::QUANT_WS_BYTES);
     char* part = wsb + bql::QUANT_WS_BYTES + align256(bql::packed_act_bytes(M, K));
     const int variant = accum == BQL_ACCUM_FAST ? bql::V_FP8 : bql::V_FP8X;
-    if (adt != BQL_E4M3 && bql::fused_small_m(M, N, K)) {
+    const bool codes = adt == BQL_E4M3 || adt == BQL_E4M3_TILES;
+    if (!codes && bql::fused_small_m(M, N, K)) {
         // one launch: the small-M kernel quantizes A itself
         bql::LinearArgs la;
         la.variant = variant;
@@ -408,18 +429,19 @@ static bql_status run_fp8_linear(const void* a, bql_dtype adt, float* a_scale, c
     const float* sa = a_scale;
     // pre-quantized A is read row-major where it is by the kernels that read
     // it that way at full speed (small M, the k-split exact tile kernel)
+    // and packed A (BQL_E4M3_TILES) where it is by every tile kernel
     const bool direct = adt == BQL_E4M3 && bql::reads_rowmajor_a(variant, M, N, K);
     hipError_t e = hipSuccess;
-    if (adt != BQL_E4M3) {
+    if (!codes) {
         e = bql::launch_quant_dynamic_packed(a, adt, M, K, aq, a_scale, wsb, s);
         sa = (const float*)(wsb + 4096);
-    } else if (!direct) {
+    } else if (adt == BQL_E4M3 && !direct) {
         e = bql::launch_pack_codes((const uint8_t*)a, M, K, aq, s);
     }
     if (e != hipSuccess) return hip_status(e);
     bql::LinearArgs la;
     la.variant = variant;
-    la.a = direct ? a : aq;
+    la.a = direct || adt == BQL_E4M3_TILES ? a : aq;
     la.a_rowmajor = direct ? 1 : 0;
     la.w = (const uint8_t*)w_packed;
     la.M = M;

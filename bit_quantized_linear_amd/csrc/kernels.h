@@ -20,6 +20,9 @@ hipError_t launch_quant_dynamic(const void* x, int xdt, int64_t numel, uint8_t* 
                                 float* scale_out, void* ws, hipStream_t stream);
 // Bytes of the packed 8-bit activation layout (16 x 128 operand tiles).
 size_t packed_act_bytes(int64_t M, int64_t K);
+// M at and below which the linears run the small-M (streaming) kernels,
+// which read A row-major; above it the tile kernels take packed A.
+constexpr int64_t SMALL_M_MAX = 16;
 // Dynamic per-tensor E4M3 of a row-major [M, K] activation, written in the
 // packed layout the linear kernels read.
 hipError_t launch_quant_dynamic_packed(const void* x, int xdt, int64_t M, int64_t K, uint8_t* xq,

@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(128 * WM * WN) void gemm_ks_kernel(LinParams p) {
 constexpr int GEMV_U = 2;       // weight k-tiles per wave per batch
 constexpr int GEMV_WAVES = 8;   // measured faster than 16 at every M = 1 Llama shape
 constexpr int MAX_SPLITS = 8;
-constexpr int SMALL_M = 16;
+constexpr int SMALL_M = (int)SMALL_M_MAX;
 constexpr int FUSED_M = 16;                // small-M fp8 calls that quantize A in-kernel
 constexpr int64_t FUSED_LDS = 48 * 1024;   // bytes of A codes a fused block may stage
 

@@ -80,8 +80,10 @@ typedef enum bql_dtype {
     BQL_E4M3 = 4,  /* OCP FP8 E4M3 (bias 7, max 448, S.1111.111 = NaN), one byte */
     BQL_I8 = 5,    /* int8 */
     BQL_I32 = 6,   /* int32 */
-    BQL_INT4 = 7   /* logical int4: two's complement nibbles, two per byte
+    BQL_INT4 = 7,  /* logical int4: two's complement nibbles, two per byte
                       along K, the low nibble holding the even k */
+    BQL_E4M3_TILES = 8 /* E4M3 activation codes [M,K] in the operand-tile
+                          layout written by bql_fp8_pack_activations */
 } bql_dtype;
 
 typedef enum bql_wfmt {
@@ -134,6 +136,21 @@ size_t bql_quantize_workspace_size(int64_t numel);
 bql_status bql_fp8_quantize_dynamic(const void* x, bql_dtype xdt, int64_t numel,
                                     uint8_t* xq, float* scale_out, void* ws,
                                     size_t ws_bytes, bql_stream stream);
+
+/* Bytes of an [M,K] E4M3 activation in the operand-tile layout:
+ * ceil(M/16) * ceil(K/128) tiles of 2048 bytes. */
+size_t bql_fp8_packed_activation_bytes(int64_t M, int64_t K);
+
+/* Row-major E4M3 activation codes [M,K] (from bql_fp8_quantize_dynamic or
+ * _static, vLLM PR #4118, "Algorithm") into the operand-tile layout the
+ * large-M fp8 GEMMs read: bql_fp8_linear then takes them with adt =
+ * BQL_E4M3_TILES, and does not repack A on every call (one quantized
+ * activation feeding several linears, such as the q, k and v projections,
+ * is packed once).  Rows past M and k past K hold zero codes.
+ * codes: [M,K] bytes; packed: bql_fp8_packed_activation_bytes(M, K) bytes.
+ * K must be a multiple of 16.  The layout is private to this library. */
+bql_status bql_fp8_pack_activations(const uint8_t* codes, int64_t M, int64_t K, void* packed,
+                                    bql_stream stream);
 
 /* Static (given-scale) quantization, the checkpoint input_scale of the
  * vLLM FP8 quantization-schema RFC (static scaling):
@@ -246,7 +263,9 @@ size_t bql_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
  *   a: [M,K].  adt = BQL_F16 or BQL_BF16: A is quantized dynamically per
  *      tensor exactly as bql_fp8_quantize_dynamic does, and if a_scale is
  *      not NULL the scale used is written there.  adt = BQL_E4M3: A already
- *      holds codes and a_scale (required) holds sA.
+ *      holds codes and a_scale (required) holds sA.  adt = BQL_E4M3_TILES:
+ *      the same codes packed by bql_fp8_pack_activations (M > 16 and
+ *      N >= 16 only, else BQL_ERR_SHAPE).
  *   w_packed/w_scale: from bql_prepack_weight in FP8_TENSOR (w_per_channel
  *      = 0, one scale) or FP8_CHANNEL (w_per_channel = 1, N scales).
  *   y: [M,N] of ydt: BQL_F16 / BQL_BF16 (round to nearest even of the fp32

@@ -103,6 +103,29 @@ def test_fp8_linear_validation(L):
     assert call(M=0, wsb=0, work=None) == OK  # no-op
 
 
+def test_packed_activation_validation(L):
+    assert L.bql_fp8_packed_activation_bytes(17, 130) == 2 * 2 * 2048
+    assert L.bql_fp8_packed_activation_bytes(0, 128) == 0
+    f = L.bql_fp8_pack_activations
+    assert f(A16, 32, 120, A16, None) == ERR_SHAPE and "multiple of 16" in _err(L)
+    assert f(A16, -1, 128, A16, None) == ERR_SHAPE
+    assert f(None, 32, 128, A16, None) == ERR_NULL
+    assert f(A16, 32, 128, None, None) == ERR_NULL
+    assert f(MIS, 32, 128, A16, None) == ERR_ALIGN
+    assert f(None, 0, 128, None, None) == OK  # no-op
+    # bql_fp8_linear with BQL_E4M3_TILES: the tile kernels only (M > 16, N >= 16)
+    g = L.bql_fp8_linear
+    ws = L.bql_fp8_linear_workspace_size(32, 64, 64)
+
+    def call(M=32, N=64, sa=A16):
+        return g(A16, 8, sa, A16, A16, 0, M, N, 64, None, A16, 2, 0, A16, ws, None)
+
+    assert call(M=16) == ERR_SHAPE and "M > 16" in _err(L)
+    assert call(N=8) == ERR_SHAPE
+    assert call(sa=None) == ERR_NULL        # packed codes need a_scale
+    assert call(M=0) == OK
+
+
 def test_fp8_linear_noalloc_validation(L):
     # same checks as bql_fp8_linear, and shapes whose scratch exceeds the
     # library's fixed array are refused before anything is launched
