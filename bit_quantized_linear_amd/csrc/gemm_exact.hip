@@ -11,16 +11,17 @@
 // fp8 -> f16 conversion is vector-ALU work on top of it.
 //
 // Organisation (gfx950: 4 SIMDs per CU, 160 KiB LDS per CU):
-//   * A block computes a 256 x 256 output tile with four waves, one per SIMD,
-//     each owning a 128 x 128 sub-tile (64 accumulators of 16 x 16, 256 fp32
-//     per lane, held in the accumulation registers).  The conversions per
-//     MFMA fall with the wave tile's size: 128 x 128 needs one fp8 -> f16
-//     pair conversion per 16 MFMA cycles.
+//   * A block computes 256 rows x 32 fn columns (fn = 2 .. 8, chosen per
+//     shape with the K split by exact_plan below).  Blocks up to 192 columns
+//     run eight waves of 64 rows, two per SIMD; wider ones four waves of 128
+//     rows, one per SIMD, each holding a 128 x 16 fn sub-tile in the
+//     accumulation registers (256 fp32 per lane at fn = 8), so that each
+//     fp8 -> f16 conversion of A feeds fn MFMAs.
 //   * Both operands are in HBM in the 16-row x 128-k operand-tile layout
 //     (weights by prepack, activations by the quantizer).  A stage of the LDS
-//     ring is one half of a k-tile (64 k) of the block's 16 A and 16 B
-//     strips, 32 KiB, moved by LDS-DMA (buffer_load ... lds, 1 KiB per wave
-//     instruction, no VGPR staging); four stages (128 KiB) are in flight.
+//     ring is one half of a k-tile (64 k) of the block's 16 A strips and its
+//     B strips, up to 32 KiB, moved by LDS-DMA (buffer_load ... lds, 1 KiB
+//     per wave instruction, no VGPR staging); four stages are in flight.
 //   * Per wave, a half-step is two MFMA k-slices of 8 k per lane.  Slice 0
 //     multiplies with the B operands decoded during the previous half-step,
 //     and meanwhile decodes B's slice 1 and reads the next half-step's raw B
@@ -42,30 +43,35 @@ namespace bql {
 
 namespace {
 
-constexpr int XB = 256;                    // block tile edge (rows and columns)
-constexpr int XW = 4;                      // waves per block (2 x 2)
-constexpr int XF = 8;                      // 16-row A strips per wave (128 rows)
-constexpr int XSTRIPS = XB / 16;           // 16-row strips per operand per block
+constexpr int XB = 256;                    // block rows
+constexpr int XSTRIPS = XB / 16;           // 16-row A strips per block
 constexpr int XS = 4;                      // LDS ring depth (stages)
-constexpr int XEPI_ROW = XF * 16 * 4 + 16; // epilogue row: up to 128 fp32 values, padded
-constexpr int XEPI_WAVE = XF / 2 * 16 * XEPI_ROW;           // 64 staged rows per wave
-constexpr int XEPI_SCALES = XW * XEPI_WAVE;                 // then 128 column scales per wave
-constexpr int XLDS_EPI = XEPI_SCALES + XW * XF * 16 * 4;
+constexpr int XCOLS = 128;                 // most columns a wave owns (8 strips)
+constexpr int XEPI_ROW = XCOLS * 4 + 16;   // epilogue row: up to 128 fp32 values, padded
 
-// Stage geometry of a block with FN 16-column B strips per wave (2 FN per
-// block).  A stage holds the block's 16 A strips and its B strips rounded up
-// to whole DMA rounds (one slot per wave per round); slots past the block's
-// B strips are loaded out of range (zeros, no memory access) and never read.
-template <int FN>
+// Geometry of a block of 256 rows x 2 FN 16-column B strips: WM waves along
+// M (each XF = 16 / WM A strips) times 2 along N (each FN B strips).  A
+// stage holds the block's 16 A strips and its B strips rounded up to whole
+// DMA rounds (one slot per wave per round); slots past the block's B
+// strips are loaded out of range (zeros, no memory access) and never read.
+template <int FN, int WM>
 struct XCfg {
+    static constexpr int XW = 2 * WM;                     // waves per block
+    static constexpr int XF = XSTRIPS / WM;               // A strips per wave
+    static constexpr int BPS = (FN + XF - 1) / XF;        // B strips a step of a slice handles
     static constexpr int BSLOTS = (2 * FN + XW - 1) / XW * XW;
     static constexpr int SLOTS = XSTRIPS + BSLOTS;
     static constexpr int STAGE = SLOTS * 1024;            // half a k-tile of every slot
     static constexpr int LD = SLOTS / XW;                 // DMA instructions per wave per stage
     static constexpr int LDS = XS * STAGE;
-    static constexpr int LDS_ALL = LDS > XLDS_EPI ? LDS : XLDS_EPI;
+    static constexpr int EPI_ROWS = XF / 2 * 16;          // rows a wave stages per epilogue pass
+    static constexpr int EPI_WAVE = EPI_ROWS * XEPI_ROW;
+    static constexpr int EPI_SCALES = XW * EPI_WAVE;      // then XCOLS column scales per wave
+    static constexpr int LDS_EPI = EPI_SCALES + XW * XCOLS * 4;
+    static constexpr int LDS_ALL = LDS > LDS_EPI ? LDS : LDS_EPI;
+    static_assert(FN <= 8 && (WM == 2 || WM == 4), "shape");
     static_assert(LD * 2 < 64 && LD <= XF, "vmcnt range; one DMA instruction per step");
-    static_assert(LDS <= XEPI_SCALES, "the column scales lie past the ring");
+    static_assert(LDS <= EPI_SCALES, "the column scales lie past the ring");
 };
 
 // Eight E4M3 codes -> eight fp16 of the same values (4 conversions).
@@ -75,7 +81,7 @@ __device__ __forceinline__ v8h dec8(uint32_t d0, uint32_t d1) { return e4m3x8_to
 // workgroup barriers (the LDS-DMA writes are not visible to the compiler).
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Scales 64 staged rows of accumulators (128 fp32 values each, XEPI_ROW
+// Scales ROWS staged rows of accumulators (16 FN fp32 values each, XEPI_ROW
 // bytes apart) by their column's sA * sW[n] (colsc), converts them to the
 // output dtype OUT and writes them with 16-byte stores: a lane handles
 // 16 / (output size) consecutive columns per store, all of a pass's stores
@@ -83,18 +89,18 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // store's columns lie all inside or all outside N.  Roundings as the other
 // kernels' epilogue: nearest even to fp16 / bf16, E4M3 of fp32(Y / output_scale).
 // RAW: the unscaled fp32 sums, into a split-K partial buffer.
-template <int OUT, int FN, bool RAW = false>
+template <int OUT, int FN, int ROWS, bool RAW = false>
 __device__ __forceinline__ void store_rows_t(const LinParams& p, void* dst, int64_t ld, const float* band,
                                              const float* colsc, int64_t rbase, int64_t col0,
                                              int lane) {
     static_assert(!RAW || OUT == OUT_F32, "partials are fp32");
     constexpr int ESZ = OUT == OUT_E4M3 ? 1 : (OUT == OUT_F32 ? 4 : 2);
-    constexpr int PER = 16 / ESZ, CHUNKS = FN * 16 / PER, ITERS = XF / 2 * 16 * CHUNKS / 64;
-    static_assert(XF / 2 * 16 * CHUNKS % 64 == 0, "whole stores per lane");
+    constexpr int PER = 16 / ESZ, CHUNKS = FN * 16 / PER, ITEMS = ROWS * CHUNKS, ITERS = (ITEMS + 63) / 64;
     const float os = OUT == OUT_E4M3 ? *p.ep.out_scale : 1.0f;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int q = lane + 64 * it;
+        if (ITEMS % 64 != 0 && q >= ITEMS) break;
         const int row = q / CHUNKS, c0 = (q % CHUNKS) * PER;
         const int64_t m = rbase + row, n = col0 + c0;
         const float* src = band + row * (XEPI_ROW / 4) + c0;
@@ -124,13 +130,14 @@ __device__ __forceinline__ void store_rows_t(const LinParams& p, void* dst, int6
 }
 
 // Instruction order of one A strip's step of a slice, for the scheduler:
-// each of its 8 MFMAs is followed by one VALU instruction (the conversions
+// each of its FN MFMAs is followed by one VALU instruction (the conversions
 // of the next operands; measured on gfx950, 16x16x32 MFMAs issue fastest
 // with one VALU instruction between consecutive ones, faster than back to
-// back), then the step's LDS read and, in slice 0, its DMA instruction.
-// Nothing moves across steps: a conversion pulled forward from a later step
-// could wait on an LDS read issued just before it.
-template <bool DMA, int FN>
+// back), then the step's other conversions, its LDS reads and, in slice 0,
+// its DMA instruction.  Nothing moves across steps: a conversion pulled
+// forward from a later step could wait on an LDS read issued just before it.
+// VALUS: the step's conversions (4 per 8-code operand).
+template <bool DMA, int FN, int VALUS, int DS>
 __device__ __forceinline__ void interleave() {
     constexpr int MFMA = 0x008, VALU = 0x002, DS_READ = 0x100, VMEM_READ = 0x020;
 #pragma unroll
@@ -138,8 +145,8 @@ __device__ __forceinline__ void interleave() {
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(VALU, 1, 0);
     }
-    if constexpr (FN < XF) __builtin_amdgcn_sched_group_barrier(VALU, XF - FN, 0);
-    __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+    if constexpr (FN < VALUS) __builtin_amdgcn_sched_group_barrier(VALU, VALUS - FN, 0);
+    __builtin_amdgcn_sched_group_barrier(DS_READ, DS, 0);
     if constexpr (DMA) __builtin_amdgcn_sched_group_barrier(VMEM_READ, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -147,13 +154,16 @@ __device__ __forceinline__ void interleave() {
 }  // namespace
 
 // FN: 16-column B strips per wave (8: 256 x 256 blocks, 7: 256 x 224, ...,
-// 4: 256 x 128).  With p.splits > 1, block column blockIdx.y takes k-tiles
-// [blockIdx.y * kt_per_split, + kt_per_split) and writes its raw fp32 sums
-// to that split's partial buffer; the split-K reduce applies the epilogue.
-template <int FN>
-__global__ __launch_bounds__(64 * XW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// 2: 256 x 64).  WM = 2: four waves of 128 rows, one per SIMD; WM = 4: eight
+// waves of 64 rows, two per SIMD (each with at most 256 registers).  With
+// p.splits > 1, block column blockIdx.y takes k-tiles [blockIdx.y *
+// kt_per_split, + kt_per_split) and writes its raw fp32 sums to that
+// split's partial buffer; the split-K reduce applies the epilogue.
+template <int FN, int WM>
+__global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(WM / 2, WM / 2)))
 void gemm_exact_kernel(LinParams p) {
-    using C = XCfg<FN>;
+    using C = XCfg<FN, WM>;
+    constexpr int XW = C::XW, XF = C::XF, BPS = C::BPS;
     constexpr int BN = 32 * FN;  // block columns
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // the wave index and the tile coordinates (whose 64-bit divisions run on
@@ -232,7 +242,7 @@ void gemm_exact_kernel(LinParams p) {
     const int64_t m0 = bm * XB + wm * XF * 16, col0 = bn * BN + wn * FN * 16;
     // sA * sW[n] of the wave's 128 output columns (one value per tensor),
     // kept in LDS past the operand ring until the epilogue
-    float* colsc = (float*)(lds + XEPI_SCALES) + wave * XF * 16;
+    float* colsc = (float*)(lds + C::EPI_SCALES) + wave * XCOLS;
     if (lane < 16) {
         const float sa = *p.ep.a_scale;
 #pragma unroll
@@ -284,21 +294,23 @@ void gemm_exact_kernel(LinParams p) {
         __builtin_amdgcn_s_barrier();
         compiler_fence();
 
-        // slice 0: MFMAs on b0; decode B slice 1; read the next raw B; one
-        // DMA instruction of stage s+3 per step
+        // slice 0: MFMAs on b0; decode B slice 1 and read the next raw B
+        // (BPS strips per step); one DMA instruction of stage s+3 per step
         v8h a = dec8(ra_[0][0], ra_[0][1]);
 #pragma unroll
         for (int i = 0; i < XF; ++i) {
             v8h an;
             if (i + 1 < XF) an = dec8(ra_[i + 1][0], ra_[i + 1][1]);
             else an = dec8(ra_[0][2], ra_[0][3]);  // slice 1's first A operand
-            if (i < FN) b1[i] = dec8(rb_[i][2], rb_[i][3]);
+#pragma unroll
+            for (int j = i * BPS; j < (i + 1) * BPS && j < FN; ++j) b1[j] = dec8(rb_[j][2], rb_[j][3]);
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = mfma_f16(a, b0[j], acc[i][j]);
-            if (i < FN) rb_[i] = read_b(s + 1, i);
+#pragma unroll
+            for (int j = i * BPS; j < (i + 1) * BPS && j < FN; ++j) rb_[j] = read_b(s + 1, j);
             issue_one(s + 3, i);
             a = an;
-            interleave<true, FN>();
+            interleave<true, FN, 4 + 4 * BPS, BPS>();
         }
         // slice 1: MFMAs on b1; read the next raw A; decode the next B slice 0
 #pragma unroll
@@ -306,11 +318,12 @@ void gemm_exact_kernel(LinParams p) {
             v8h an = a;
             if (i + 1 < XF) an = dec8(ra_[i + 1][2], ra_[i + 1][3]);
             ra_[i] = read_a(s + 1, i);
-            if (i < FN) b0[i] = dec8(rb_[i][0], rb_[i][1]);
+#pragma unroll
+            for (int j = i * BPS; j < (i + 1) * BPS && j < FN; ++j) b0[j] = dec8(rb_[j][0], rb_[j][1]);
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = mfma_f16(a, b1[j], acc[i][j]);
             a = an;
-            interleave<false, FN>();
+            interleave<false, FN, 4 + 4 * BPS, 1>();
         }
     };
     // the last half-step is written out after the loop: with it inside, the
@@ -318,14 +331,14 @@ void gemm_exact_kernel(LinParams p) {
     for (int s = 0; s + 1 < H; ++s) half_step(s);
     half_step(H - 1);
 
-    // ---- epilogue, in two passes of 64 rows per wave: the fp32
+    // ---- epilogue, in two passes of half the wave's rows: the fp32
     // accumulators are staged in LDS straight from the accumulation
     // registers (compile-time indices), then scaled by their column's
     // sA * sW[n], converted and written with 16-byte stores
     wait_vmcnt<0>();
     compiler_fence();
     __syncthreads();
-    float* band = (float*)(lds + wave * XEPI_WAVE);
+    float* band = (float*)(lds + wave * C::EPI_WAVE);
     auto stage = [&](auto ib_tag) __attribute__((always_inline)) {
         constexpr int IB = decltype(ib_tag)::value;
 #pragma unroll
@@ -343,11 +356,11 @@ void gemm_exact_kernel(LinParams p) {
         constexpr bool RAW = decltype(raw_tag)::value;
         stage(std::integral_constant<int, 0>{});
         __builtin_amdgcn_wave_barrier();
-        store_rows_t<OUT, FN, RAW>(p, dst, ld, band, colsc, m0, col0, lane);
+        store_rows_t<OUT, FN, C::EPI_ROWS, RAW>(p, dst, ld, band, colsc, m0, col0, lane);
         __builtin_amdgcn_wave_barrier();
         stage(std::integral_constant<int, XF / 2>{});
         __builtin_amdgcn_wave_barrier();
-        store_rows_t<OUT, FN, RAW>(p, dst, ld, band, colsc, m0 + XF / 2 * 16, col0, lane);
+        store_rows_t<OUT, FN, C::EPI_ROWS, RAW>(p, dst, ld, band, colsc, m0 + C::EPI_ROWS, col0, lane);
     };
     if (p.splits > 1) {
         float* part = (float*)p.partial + (int64_t)blockIdx.y * p.M * p.N;
@@ -365,9 +378,9 @@ void gemm_exact_kernel(LinParams p) {
     }
 }
 
-template <int FN>
+template <int FN, int WM>
 static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
-    using C = XCfg<FN>;
+    using C = XCfg<FN, WM>;
     // dynamic LDS above 64 KiB needs the attribute, set once per device
     // (before any graph capture: the first launch is eager)
     static std::atomic<uint64_t> configured{0};
@@ -376,13 +389,13 @@ static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const uint64_t bit = uint64_t(1) << (dev & 63);
     if (!(configured.load(std::memory_order_acquire) & bit)) {
-        e = hipFuncSetAttribute((const void*)gemm_exact_kernel<FN>,
+        e = hipFuncSetAttribute((const void*)gemm_exact_kernel<FN, WM>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_ALL);
         if (e != hipSuccess) return e;
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
     const int64_t blocks = ((p.M + XB - 1) / XB) * ((p.N + 32 * FN - 1) / (32 * FN));
-    gemm_exact_kernel<FN><<<dim3((unsigned)blocks, (unsigned)p.splits), 64 * XW, C::LDS_ALL, stream>>>(p);
+    gemm_exact_kernel<FN, WM><<<dim3((unsigned)blocks, (unsigned)p.splits), 64 * C::XW, C::LDS_ALL, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -423,14 +436,17 @@ ExactPlan exact_plan(int64_t M, int64_t N, int64_t K) {
     return best;
 }
 
-hipError_t launch_gemm_exact(const LinParams& p, int fn, hipStream_t stream) {
-    switch (fn) {
-        case 8: return launch_fn<8>(p, stream);
-        case 7: return launch_fn<7>(p, stream);
-        case 6: return launch_fn<6>(p, stream);
-        case 4: return launch_fn<4>(p, stream);
-        case 3: return launch_fn<3>(p, stream);
-        case 2: return launch_fn<2>(p, stream);
+// Blocks of 256 x 64 .. 256 x 192 run eight waves (two per SIMD), wider
+// ones four: measured on MI355X at M = 1024 and 4096, eight waves are 1-12 %
+// faster for fn <= 6 and up to 2.5 % slower for fn = 7 and 8.
+hipError_t launch_gemm_exact(const LinParams& p, const ExactPlan& plan, hipStream_t stream) {
+    switch (plan.fn) {
+        case 8: return launch_fn<8, 2>(p, stream);
+        case 7: return launch_fn<7, 2>(p, stream);
+        case 6: return launch_fn<6, 4>(p, stream);
+        case 4: return launch_fn<4, 4>(p, stream);
+        case 3: return launch_fn<3, 4>(p, stream);
+        case 2: return launch_fn<2, 4>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -1281,7 +1281,7 @@ static hipError_t run_gemm_kernel(const LinParams& p, hipStream_t stream) {
         // M >= 256: the 128-row-per-wave kernel (half the conversions per
         // MFMA of the 64x64-per-wave kernels), with its K splits
         const ExactPlan xp = exact_plan(p.M, p.N, p.K);
-        if (xp.fn != 0) return launch_gemm_exact(p, xp.fn, stream);
+        if (xp.fn != 0) return launch_gemm_exact(p, xp, stream);
         // at most one 128x128 tile per CU: a four-stage ring, so that each
         // k-tile's DMA has three k-tiles of compute to land behind
         if (uses_ks(V, p.M, p.N, p.K)) return launch_gemm_ks<128, 128, 2, 2, 4>(p, stream);

@@ -224,8 +224,8 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t nbm, int64_t nbn,
     bn = rem / gm;
 }
 
-// The exact fp8 tile kernel (256-row blocks of 4 waves, each wave 128 rows
-// by fn 16-column strips); defined in gemm_exact.hip.  exact_plan gives its
+// The exact fp8 tile kernel (256-row blocks of four waves of 128 rows, or
+// eight of 64 rows, each by fn 16-column strips); defined in gemm_exact.hip.  exact_plan gives its
 // block width (fn 0: the kernel is not used at this shape) and K splits;
 // launch_gemm_exact takes p.splits and p.kt_per_split as planned.
 struct ExactPlan {
@@ -233,7 +233,7 @@ struct ExactPlan {
     int splits;
 };
 ExactPlan exact_plan(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_exact(const LinParams& p, int fn, hipStream_t stream);
+hipError_t launch_gemm_exact(const LinParams& p, const ExactPlan& plan, hipStream_t stream);
 
 // Launch of the per-group W4A16 tile kernel (128 x 256 blocks, one 128 x 64
 // output tile per wave); defined in gemm_w4a16.hip.  w4a16_tile_fits tells
