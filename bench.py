@@ -931,7 +931,7 @@ def main():
                 **({} if fast else {"frac_of_f16_mfma_peak": round(ach / PEAK_F16_TFLOPS, 4)}),
                 "algorithmic_bytes_per_launch": algorithmic_bytes_gemm(M, N, K),
                 "kernel": (f"gemm_kernel<V_FP8,256,256,4,4,2> M={M} N={N} K={K}" if fast else
-                           f"gemm_exact_kernel<7> (256x224 tiles) M={M} N={N} K={K}"),
+                           f"gemm_exact_kernel<7, 2> (256x224 blocks, four waves) M={M} N={N} K={K}"),
                 "avg_launch_us": round(us, 2), "flops_per_launch": fl}
     log("kernel rooflines ...")
     roof = kernel_roofline(False)
