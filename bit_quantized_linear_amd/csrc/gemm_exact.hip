@@ -401,20 +401,21 @@ static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
 
 // Block width (fn strips of 16 columns per wave) and K splits for a shape,
 // from a cost model in microseconds fitted to timings of every (fn, splits)
-// at M = 256 .. 4096 on Llama-shaped N x K (MI355X).  One block per CU at a
+// at M = 200 .. 4096 on Llama-shaped N x K (MI355X).  One block per CU at a
 // time, so a launch takes full rounds of CUS blocks and a tail round (whose
 // k-tiles run a little faster: fewer busy CUs, higher clock); a k-tile of a
 // block costs a fixed part (the A side: its 16 strips' DMA, reads and
 // conversions) and a part per B strip; K splits add the fp32 partials'
-// write and read and the reduce launch.  Below M = 513 the 128-row kernels
-// measured as fast or faster.
+// write and read and the reduce launch.  At M = 128 (one 128-row tile) the
+// 128-row kernels measured 6-19 % faster; from M = 200 up this kernel was as
+// fast or faster (up to 32 % at M = 512, N = 28672).
 ExactPlan exact_plan(int64_t M, int64_t N, int64_t K) {
     constexpr int64_t CUS = 256;
     constexpr double KTILE_US = 0.76, KTILE_US_PER_FN = 0.25, BLOCK_US = 1.3, TAIL_SPEED = 0.95;
     constexpr double PARTIAL_BYTES_PER_US = 6.0e6, REDUCE_US = 6.0;
     constexpr int FNS[] = {8, 7, 6, 4, 3, 2};
     ExactPlan best{0, 1};
-    if (M <= 512) return best;
+    if (M <= 128) return best;
     const int64_t KT = (K + 127) / 128, mt = (M + XB - 1) / XB;
     double best_us = 0;
     for (int fn : FNS) {

@@ -1200,7 +1200,7 @@ static hipError_t launch_gemm_ks(const LinParams& p, hipStream_t stream) {
 // three-stage ring; shapes with many 256x256 tiles favour the big fp8 tile.
 constexpr int64_t CUS = 256;
 // Exact fp8 runs the 256-row kernel of gemm_exact.hip where exact_plan
-// takes the shape (M >= 256); below that, with at most one 128x128 output
+// takes the shape (M > 128); below that, with at most one 128x128 output
 // tile per CU, the k-split kernel.
 static bool uses_ks(int variant, int64_t M, int64_t N, int64_t K) {
     return variant == V_FP8X && exact_plan(M, N, K).fn == 0 && ((M + 127) / 128) * ((N + 127) / 128) <= CUS;
@@ -1280,8 +1280,8 @@ static hipError_t run_gemm_kernel(const LinParams& p, hipStream_t stream) {
     const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
     if constexpr (V == V_FP8X) {
-        // M >= 256: the 128-row-per-wave kernel (half the conversions per
-        // MFMA of the 64x64-per-wave kernels), with its K splits
+        // M > 128: the 256-row kernel (at least four times the MFMAs per
+        // A conversion of the 64x64-per-wave kernels), with its K splits
         const ExactPlan xp = exact_plan(p.M, p.N, p.K);
         if (xp.fn != 0) return launch_gemm_exact(p, xp, stream);
         // at most one 128x128 tile per CU: a four-stage ring, so that each

@@ -120,13 +120,13 @@ def exact_plan(M: int, N: int, K: int) -> tuple:
     """(fn, splits) of the exact fp8 tile kernel for an M x N x K linear:
     blocks of 256 rows x 32 fn columns (each wave 128 rows x fn 16-column
     strips), K split `splits` ways; (0, 1) where the 128-row kernels run
-    (M <= 512).  The library's cost model in microseconds: rounds of 256
+    (M <= 128).  The library's cost model in microseconds: rounds of 256
     blocks (one per CU), a tail round a little faster, a k-tile costing
     0.76 + 0.25 fn, 1.3 per block, and for K splits the fp32 partials at
     6 MB/us plus 6 for the reduce.  test_abi_host checks the split counts
     against the library's workspace sizes."""
     best, best_us = (0, 1), None
-    if M <= 512:
+    if M <= 128:
         return best
     KT, mt = (K + 127) // 128, (M + 255) // 256
     for fn in (8, 7, 6, 4, 3, 2):

@@ -1,4 +1,4 @@
-"""GPU parity of the exact fp8 tile kernel for M > 512 (blocks of 256 rows
+"""GPU parity of the exact fp8 tile kernel for M > 128 (blocks of 256 rows
 by 32 fn columns, each wave 128 rows by fn 16-column strips, K split over
 blocks where the planner says so), against the CPU oracle.
 

@@ -1,10 +1,11 @@
 """GPU parity of the tile kernels with K split over blocks, against the CPU
 oracle.
 
-Shapes with few 128 x 128 output tiles (M of a few hundred rows) split K
-over blocks: each split's raw sums (fp32, or the exact int32 of W4A8) go to
-a partial buffer and a fixed-order reduce applies the epilogue.  Covered:
-the exact fp8 k-split kernel (dynamic and pre-quantized row-major E4M3 A,
+Shapes with few output tiles (M of a few hundred rows) split K over
+blocks: each split's raw sums (fp32, or the exact int32 of W4A8) go to a
+partial buffer and a fixed-order reduce applies the epilogue.  Covered:
+the exact fp8 kernels with K split (the k-split kernel at M <= 128, the
+256-row tile kernel above; dynamic and pre-quantized row-major E4M3 A,
 per-channel weights, fp8 output with an output_scale), the fast fp8 kernel
 (against its derived bound), W4A8 per channel (int32 accumulators bit for
 bit) and per group, and ragged M / N.  The linears are those of vLLM PR
