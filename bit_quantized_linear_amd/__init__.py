@@ -368,16 +368,21 @@ def fp8_linear_noalloc(a: torch.Tensor, pw: PackedWeight, a_scale: Optional[torc
                        out: Optional[torch.Tensor] = None, fast_accum: bool = False) -> torch.Tensor:
     """fp8_linear on the library's own per-GPU scratch: no workspace argument
     and no allocation inside the call (`out` may be given so that the call
-    allocates nothing at all).  Calls overlapping on one GPU race."""
+    allocates nothing at all).  Calls overlapping on one GPU race.  `a` as
+    for fp8_linear, PackedActivations included."""
+    if isinstance(a, PackedActivations):
+        M, K, adt, a = a.M, a.K, E4M3_TILES, a.packed
+    else:
+        M, K = a.shape
+        adt = _TORCH_TO_BQL[a.dtype]
     _need_cuda(a, a_scale, output_scale, out)
     L = lib()
-    M, K = a.shape
     N = pw.N
     ydt = _TORCH_TO_BQL[out_dtype]
     if out is None:
         out = torch.empty((M, N), dtype=torch.uint8 if ydt == E4M3 else out_dtype, device=a.device)
     _check("bql_fp8_linear_noalloc",
-           L.bql_fp8_linear_noalloc(_ptr(a), _TORCH_TO_BQL[a.dtype], _ptr(a_scale), _ptr(pw.packed),
+           L.bql_fp8_linear_noalloc(_ptr(a), adt, _ptr(a_scale), _ptr(pw.packed),
                                     _ptr(pw.scales), int(pw.per_channel), M, N, K,
                                     _ptr(output_scale), _ptr(out), ydt, int(bool(fast_accum)),
                                     _stream(a.device)))

@@ -3,7 +3,8 @@
 Every path is captured once (small-M fused and split-K, the tiled kernel,
 exact and fast accumulation, W8A16, W4A8, the static-scale linear, the
 small-N linear, the fused RMSNorm quantizers, per-group W4A8, pre-quantized
-A read row-major by the k-split kernel) and replayed
+A read row-major by the k-split kernel, pre-packed A into the exact tile
+kernel with K split) and replayed
 several times with eager work and synchronizations in between; each replay
 must equal the eager output bit for bit (all kernels are deterministic).
 """
@@ -42,8 +43,11 @@ def _replays_match(run, out, noise):
 
 
 @pytest.mark.parametrize("fast", [False, True])
+# (1024, 4096, 4096) and (300, 2048, 4096): the exact tile kernel with eight
+# waves, the latter with K split; (520, 4208, 8000): four waves, K split
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (3, 1024, 1024), (16, 1024, 1024), (8, 4096, 4096),
-                                   (1024, 4096, 4096), (130, 272, 400)])
+                                   (1024, 4096, 4096), (130, 272, 400), (300, 2048, 4096),
+                                   (520, 4208, 8000)])
 def test_fp8_linear_graph(M, N, K, fast):
     g = wl.rng(11, M, N)
     pw = bql.prepack_weight(dev16(wl.weight(g, N, K, "bf16"), "bf16"), "fp8_tensor")
@@ -146,10 +150,10 @@ def test_w4a8_group_graph(M):
                    lambda: bql.w4a8_group_linear(aq, sa * 2, pw))
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 1024, 1040), (64, 272, 400)])
+@pytest.mark.parametrize("M,N,K", [(100, 1024, 1040), (64, 272, 400)])
 def test_prequantized_ksplit_graph(M, N, K):
-    # E4M3 A at M > 16 with few output tiles: the k-split kernel gathers A
-    # row-major where it is (no repack launch); ragged K
+    # E4M3 A at 16 < M <= 128 with few output tiles: the k-split kernel
+    # gathers A row-major where it is (no repack launch); ragged K
     g = np.random.Generator(np.random.PCG64(M + K))
     codes = g.integers(0, 256, (M, K), dtype=np.uint8)
     codes[(codes & 0x7F) == 0x7F] = 0x38
@@ -161,3 +165,20 @@ def test_prequantized_ksplit_graph(M, N, K):
     other = torch.empty_like(out)
     _replays_match(lambda: bql.fp8_linear(a, pw, a_scale=sa, out_dtype=torch.bfloat16, out=out, ws=ws),
                    out, lambda: bql.fp8_linear(a, pw, a_scale=sa * 2, out_dtype=torch.bfloat16, out=other))
+
+
+def test_packed_activations_graph():
+    # pre-packed E4M3 A (BQL_E4M3_TILES) into the exact tile kernel, K split
+    M, N, K = 520, 4208, 8000
+    g = np.random.Generator(np.random.PCG64(M + N + K))
+    codes = g.integers(0, 256, (M, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    pw = bql.prepack_weight(dev16(wl.weight(wl.rng(19, N), N, K, "bf16"), "bf16"), "fp8_tensor")
+    pa = bql.pack_activations(dev(codes))
+    sa = torch.tensor([0.02], dtype=torch.float32, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(256, bql.fp8_linear_workspace_size(M, N, K)), dtype=torch.uint8, device=DEV)
+    other = torch.empty_like(out)
+    _replays_match(lambda: bql.fp8_linear(pa, pw, a_scale=sa, out_dtype=torch.bfloat16, out=out, ws=ws),
+                   out, lambda: bql.fp8_linear(pa, pw, a_scale=sa * 2, out_dtype=torch.bfloat16, out=other))
+

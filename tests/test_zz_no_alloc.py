@@ -82,6 +82,23 @@ def test_noalloc_prequantized_per_channel_fp8_out():
             assert_close(host_f64(y_na)[rows], y_ref, f"noalloc prequantized M={M}")
 
 
+def test_noalloc_packed_activations():
+    # pre-packed E4M3 A (BQL_E4M3_TILES) through the exact tile kernel with
+    # K split, then a smaller call at a narrower block width
+    for step, (M, N, K) in enumerate([(520, 4208, 8000), (300, 2048, 4096)]):
+        say(f"noalloc packed step {step}: M={M} N={N} K={K}")
+        W, pw, a, aq_ref, sa_ref = _case(M, N, K, 50 + step)
+        q, sa = bql.quantize_dynamic(a)
+        pa = bql.pack_activations(q)
+        y_ws = bql.fp8_linear(pa, pw, a_scale=sa, out_dtype=torch.bfloat16)
+        y_na = bql.fp8_linear_noalloc(pa, pw, a_scale=sa, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y_na), host(y_ws)), "outputs differ from bql_fp8_linear"
+        rows = rows_for(M, 450 + M, 16)
+        y_ref = oracle.fp8_linear(aq_ref, sa_ref, W.codes, W.scales, rows=rows)
+        assert_close(host_f64(y_na)[rows], y_ref, f"noalloc packed M={M}")
+
+
 def test_noalloc_refuses_oversized_call():
     M, N, K = 8192, 4096, 8192
     assert bql.fp8_linear_workspace_size(M, N, K) > bql.NOALLOC_SCRATCH_BYTES
