@@ -194,7 +194,7 @@ void gemm_exact_kernel(LinParams p) {
 
     // Half-step s = k-tile kt0 + s/2, half s%2, goes to ring slot s % XS.
     // Slot q of a stage holds A strip q (q < 16) or B strip q - 16; wave w
-    // moves slots w + 4 i, i < LD: four A strips, then its B strips.  The first
+    // moves slots w + XW i, i < LD: its A strips, then its B strips.  The first
     // stages are issued whole (issue), the later ones one instruction per
     // step of the main loop (issue_one), also past the last stage: those get
     // an out-of-range offset (zeros, no memory access) into a slot nothing
