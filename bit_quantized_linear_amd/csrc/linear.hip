@@ -99,15 +99,22 @@ struct ALoader {
 // slice its K split needs into LDS as [M][slice] codes.  One launch instead
 // of amax, cast and GEMV.
 // With a static scale (p.given_scale) the amax is skipped.
+// Fused blocks of two strips request both register sets' first batches
+// before the prologue (measured 4 % faster at M = 1, N = 28672, K = 4096;
+// with one strip per block it measured 1-11 % slower at N = 4096 and 6144).
+constexpr bool gemv_early_batches(bool fused, int nt) { return fused && nt == 2; }
+
 // Occupancy the small-M kernels are compiled for (waves per SIMD): enough
 // register room for two weight batches, A and the decoded operands without
-// spilling, and as many resident blocks as that leaves.
-constexpr int gemv_min_waves(int v, bool fused) {
+// spilling (both batches held through the fused prologue need 5), and as
+// many resident blocks as that leaves.
+constexpr int gemv_min_waves(int v, bool fused, int nt) {
+    if (gemv_early_batches(fused, nt)) return 5;
     return (fused || v == V_FP8 || v == V_W4A8) ? 6 : 5;  // V_W8A16, V_W4A8G, V_W4A16G: 5
 }
 
 template <int V, int NT, int WAVES, int U, bool FUSED>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv_min_waves(V, FUSED), 8))) void gemv_kernel(LinParams p) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv_min_waves(V, FUSED, NT), 8))) void gemv_kernel(LinParams p) {
     using Acc = typename VT<V>::Acc;
     constexpr int BT = VT<V>::B_TILE;
     extern __shared__ __attribute__((aligned(16))) uint8_t aq_lds[];
@@ -179,9 +186,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
         }
     }
     // The first batch of weights is requested next, so its HBM latency
-    // overlaps the scale computation and the A cast below.
+    // overlaps the scale computation and the A cast below (with early
+    // batches, the second register set's batch too).
+    constexpr bool EARLY = gemv_early_batches(FUSED, NT);
     u4 bq[U][NT][VT<V>::B_CHUNKS];
+    u4 bo[U][NT][VT<V>::B_CHUNKS];
     load_batch(kt_begin + wave, bq);
+    if constexpr (EARLY) load_batch(kt_begin + wave + WAVES * U, bo);
 
     float sa = 1.0f;
     if constexpr (FUSED) {
@@ -278,8 +289,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
     // Every load is unconditional (tiles past this split's range read as zero
     // without touching memory): a branch around a load makes the compiler
     // wait for all outstanding loads at the join.
-    auto step = [&](int64_t kt, const u4 (&cur)[U][NT][VT<V>::B_CHUNKS], u4 (&nxt)[U][NT][VT<V>::B_CHUNKS]) {
-        u4 a[U][VT<V>::A_CHUNKS];
+    auto load_a = [&](int64_t kt, u4 (&a)[U][VT<V>::A_CHUNKS]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = kt + u * WAVES;
@@ -296,18 +306,35 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
                 aload.load(a[u], k);
             }
         }
-        load_batch(kt + WAVES * U, nxt);
-        // keep the loads above the multiplies (the scheduler would sink them)
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto multiply = [&](const u4 (&a)[U][VT<V>::A_CHUNKS], const u4 (&cur)[U][NT][VT<V>::B_CHUNKS]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < NT; ++j) mma<V>(acc[j], a[u], cur[u][j]);
     };
+    auto step = [&](int64_t kt, const u4 (&cur)[U][NT][VT<V>::B_CHUNKS], u4 (&nxt)[U][NT][VT<V>::B_CHUNKS]) {
+        u4 a[U][VT<V>::A_CHUNKS];
+        load_a(kt, a);
+        load_batch(kt + WAVES * U, nxt);
+        // keep the loads above the multiplies (the scheduler would sink them)
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(a, cur);
+    };
     // Two steps per trip; the second may lie past the split's range, where
-    // both operands read as zero.
-    u4 bo[U][NT][VT<V>::B_CHUNKS];
-    for (int64_t kt = kt_begin + wave; kt < kt_end; kt += 2 * WAVES * U) {
+    // both operands read as zero.  With early batches the first trip's
+    // first step has its batch already requested and loads nothing.
+    int64_t kt0 = kt_begin + wave;
+    if constexpr (EARLY) {
+        if (kt0 < kt_end) {
+            u4 a[U][VT<V>::A_CHUNKS];
+            load_a(kt0, a);
+            multiply(a, bq);
+            step(kt0 + WAVES * U, bo, bq);
+        }
+        kt0 += 2 * WAVES * U;
+    }
+    for (int64_t kt = kt0; kt < kt_end; kt += 2 * WAVES * U) {
         step(kt, bq, bo);
         step(kt + WAVES * U, bo, bq);
     }

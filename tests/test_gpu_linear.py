@@ -86,15 +86,19 @@ def test_cfg3_llama3_8b(idx, M):
     _fp8_case(3, idx, M, N, K, "bf16", False, "channels", torch.bfloat16)
 
 
+@pytest.mark.parametrize("K", [256, 1200])
 @pytest.mark.parametrize("M", [1, 3, 16])
-def test_small_m_two_strip_blocks_odd_count(M):
+def test_small_m_two_strip_blocks_odd_count(M, K):
     """N = 16400: 1025 channel strips, above the count where the small-M fp8
     kernel gives each block two strips, so the last block has one; dynamic
-    quantization (fused into the GEMV for M <= 4 and, at this short K,
-    M = 16), then pre-quantized A (row-major)."""
-    _fp8_case(3, 7, M, 16400, 256, "bf16", False, "channels", torch.bfloat16)
-    g = np.random.Generator(np.random.PCG64(54 + M))
-    N, K = 16400, 256
+    quantization (fused into the GEMV for M <= 4 and, at K = 256, M = 16),
+    then pre-quantized A (row-major).  The fused two-strip blocks request
+    two k-tiles per wave before the prologue: K = 256 leaves six of the
+    eight waves without a k-tile, K = 1200 (ten k-tiles, the last ragged)
+    gives two waves a second one."""
+    _fp8_case(3, 7 if K == 256 else 8, M, 16400, K, "bf16", False, "channels", torch.bfloat16)
+    g = np.random.Generator(np.random.PCG64(54 + M + K))
+    N = 16400
     aq = _random_codes(g, (M, K))
     wq = _random_codes(g, (N, K))
     sa, sw = np.float32(0.5), np.float32(0.25)
