@@ -43,8 +43,8 @@ PEAK_F16_TFLOPS = 2500.0
 PEAK_I8_TOPS = 5000.0
 SHAPES = wl.CFG3_SHAPES
 ROTATE_BYTES = 640 * 2 ** 20  # > 2 x 256 MiB Infinity Cache
-# steps per captured graph for the microsecond-scale small-M steps (M=1024
-# steps keep one per graph; a graph launch costs several microseconds)
+# steps per captured graph for the microsecond-scale small-M steps (a graph
+# launch costs several microseconds)
 SMALL_STEPS_PER_GRAPH = 4
 # warm-up before each timed leg, in seconds of device time at least (the
 # headline steps; the other legs and the per-configuration rows)
@@ -355,6 +355,18 @@ def rotation(pw, bql, nbytes):
     return [bql.PackedWeight(pw.packed.clone(), pw.scales.clone(), pw.N, pw.K, pw.fmt) for _ in range(n)]
 
 
+def steps_per_graph(M, steps):
+    """Steps per captured graph: SMALL_STEPS_PER_GRAPH for the small-M
+    steps; otherwise the largest of 4, 2, 1 that divides the timed step count
+    (so exactly that many steps are timed).  Consecutive replays of a graph
+    leave a gap of a few microseconds on the device: at one step per graph
+    the M = 1024 step measured 1.2 % slower than at four, a 20-30 us call
+    10-15 % slower."""
+    if M <= 16:
+        return SMALL_STEPS_PER_GRAPH
+    return next(g for g in (4, 2, 1) if steps % g == 0)
+
+
 def timed_graphs(step, nslots, steps, warmup, per_graph=1, min_warm_s=ROW_WARM_S):
     return graph_step_time(step, nslots, steps, warmup, per_graph, min_warm_s)
 
@@ -420,7 +432,7 @@ def bench_w4a8(bql, dev, steps, warmup):
             for j in range(len(shapes)):
                 r = rots[j]
                 bql.w4a8_linear(aqs[j], sas[j], r[i % len(r)], out=ys[j], ws=wss[j])
-        sec = timed_graphs(step, nslots, steps, warmup, per_graph=1 if M > 16 else SMALL_STEPS_PER_GRAPH)
+        sec = timed_graphs(step, nslots, steps, warmup, per_graph=steps_per_graph(M, steps))
         ops = sum(2 * M * n * n for n in shapes)
         byts = sum(n * n // 2 + M * n + 4 * M + 2 * n + 2 * M * n for n in shapes)
         if M == 1:
@@ -476,7 +488,7 @@ def bench_int4_group(bql, dev, steps, warmup, fp16_act=False):
                     bql.w4a16_group_linear(acts[j], r[i % len(r)], out=ys[j], ws=wss[j])
                 else:
                     bql.w4a8_group_linear(acts[j][0], acts[j][1], r[i % len(r)], out=ys[j], ws=wss[j])
-        sec = timed_graphs(step, nslots, steps, warmup, per_graph=1 if M > 16 else SMALL_STEPS_PER_GRAPH)
+        sec = timed_graphs(step, nslots, steps, warmup, per_graph=steps_per_graph(M, steps))
         ops = sum(2 * M * n * n for n in shapes)
         abytes = (lambda n: 2 * M * n) if fp16_act else (lambda n: M * n + 4 * M)
         byts = sum(n * n // 2 + n * (n // 128) * 4 + abytes(n) + 2 * M * n for n in shapes)
@@ -645,8 +657,8 @@ def bench_configs(bql, dev, steps, warmup, oracle_sample_rows):
     import oracle
     out = []
 
-    def time_call(fn, nslots, small):
-        return timed_graphs(fn, nslots, steps, warmup, per_graph=SMALL_STEPS_PER_GRAPH if small else 1)
+    def time_call(fn, nslots, M):
+        return timed_graphs(fn, nslots, steps, warmup, per_graph=steps_per_graph(M, steps))
 
     def act_copies(t, nbytes):
         n = max(1, -(-ROTATE_BYTES // nbytes)) if nbytes >= 16 * 2 ** 20 else 1
@@ -696,7 +708,7 @@ def bench_configs(bql, dev, steps, warmup, oracle_sample_rows):
                         fn = (lambda i, y=y: bql.fp8_linear(acopies[i % len(acopies)], wrot[i % len(wrot)],
                                                             out=y, out_dtype=tdt, ws=ws))
                         ysz = 2
-                    sec = time_call(fn, max(len(acopies), len(wrot)), M <= 16)
+                    sec = time_call(fn, max(len(acopies), len(wrot)), M)
                     byts = N * K + 2 * M * K + ysz * M * N + 4 * (N if per_channel else 1) + 4
                     flops = 2 * M * N * K
                     row = {"config": name, "N": N, "K": K, "M": M, "out": kind if kind == "fp8" else dtype,
@@ -737,7 +749,7 @@ def bench_configs(bql, dev, steps, warmup, oracle_sample_rows):
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         ws = torch.empty(max(256, bql.lib().bql_w8a16_linear_workspace_size(M, N, K)), dtype=torch.uint8,
                          device=dev)
-        sec = time_call(lambda i: bql.w8a16_linear(a, wrot[i % len(wrot)], out=y, ws=ws), len(wrot), True)
+        sec = time_call(lambda i: bql.w8a16_linear(a, wrot[i % len(wrot)], out=y, ws=ws), len(wrot), M)
         t0 = time.perf_counter()
         oracle.w8a16_linear(oracle.decode_input(abits, "f16"), wq, s32)
         oracle_s = time.perf_counter() - t0
@@ -762,8 +774,7 @@ def bench_configs(bql, dev, steps, warmup, oracle_sample_rows):
             y = torch.empty((M, n), dtype=torch.float16, device=dev)
             ws = torch.empty(max(256, bql.lib().bql_w4a8_linear_workspace_size(M, n, n)), dtype=torch.uint8,
                              device=dev)
-            sec = time_call(lambda i: bql.w4a8_linear(aq, sa, wrot[i % len(wrot)], out=y, ws=ws), len(wrot),
-                            M <= 16)
+            sec = time_call(lambda i: bql.w4a8_linear(aq, sa, wrot[i % len(wrot)], out=y, ws=ws), len(wrot), M)
             rows = oracle_rows(M, oracle_sample_rows)
             t0 = time.perf_counter()
             aq_ref, sa_ref = oracle.int8_quant_per_token(oracle.decode_input(abits, "f16"))
@@ -891,7 +902,7 @@ def main():
         if timed:
             sec_eager = time_steps(step, args.steps, args.warmup, WARM_S)
             sec = graph_step_time(step, nslots, args.steps, args.warmup,
-                                  per_graph=1 if M > 16 else SMALL_STEPS_PER_GRAPH)
+                                  per_graph=steps_per_graph(M, args.steps))
         flops = sum(2 * M * N * K for N, K in SHAPES)
         byts = sum(algorithmic_bytes(M, N, K) for N, K in SHAPES)
         return abits, pre, outs, wss, (sec, sec_eager), flops, byts, len(asets)
@@ -992,8 +1003,8 @@ def main():
                         "exact fp32 accumulation, bf16 out",
             "M": M, "accum": "exact", "weight_rotation_copies": nrot,
             "activation_rotation_copies": a_copies,
-            "timing": "HIP graph replay of whole steps, one step per graph at M=1024 and "
-                      f"{SMALL_STEPS_PER_GRAPH} consecutive steps per graph at M=1 (each on its own "
+            "timing": f"HIP graph replay of whole steps, {steps_per_graph(M, args.steps)} consecutive "
+                      f"steps per graph at M=1024 and {SMALL_STEPS_PER_GRAPH} at M=1 (each on its own "
                       "weight copy); eager-launch rates under 'eager'",
         },
         "eager": {"value": round(flops / sec_eager / 1e12, 2), "unit": "TFLOP/s",
