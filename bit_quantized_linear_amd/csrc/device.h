@@ -134,6 +134,30 @@ __device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
     return c | (a != a ? 1u : 0u) | (b != b ? 0x100u : 0u);
 }
 
+// A data type as a compile-time argument of a generic lambda.
+template <int D>
+struct DtTag {
+    static constexpr int value = D;
+};
+
+// E4M3 codes of xa / s and xb / s (first in bits 0-7) for finite xa, xb:
+// the quotient as div_by_scale forms it (y = 1/s), clamped to [-448, 448]
+// with med3 and given the sign of x, then the nearest-even conversion.  For
+// finite inputs these are the codes of e4m3_encode2(div_by_scale(xa, s, y),
+// div_by_scale(xb, s, y)) with three instructions per value fewer (one sign
+// transfer and the NaN test).  The dynamic quantizers take it only where
+// recip_div_ok(s) holds: s = amax / 448 is then finite, and a NaN or an
+// infinity anywhere in the tensor would have made amax non-finite.
+__device__ __forceinline__ uint32_t e4m3_div2_finite(float xa, float xb, float s, float y) {
+    auto quot = [&](float x) {
+        const float q = x * y;
+        return __builtin_fmaf(__builtin_fmaf(-q, s, x), y, q);
+    };
+    const float ca = __builtin_copysignf(__builtin_amdgcn_fmed3f(quot(xa), -448.0f, 448.0f), xa);
+    const float cb = __builtin_copysignf(__builtin_amdgcn_fmed3f(quot(xb), -448.0f, 448.0f), xb);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+}
+
 // ------------------------------------------------------------- reductions
 //
 // Wave folds use DPP lane moves inside each 16-lane row: quad_perm

@@ -225,30 +225,30 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
         // x / sA as the standalone quantizer forms it: from the reciprocal
         // with one residual correction where that is the IEEE quotient's code
         // for every input (the scale's range check), else the IEEE division.
-        auto codes8 = [&](const u4& v, auto div) {
+        // enc2(a, b) gives the code pair of a / sA and b / sA; the input type
+        // is a template argument (DT), so each value converts in one step.
+        auto codes8 = [&](const u4& v, auto enc2, auto dt) {
+            constexpr int DT = decltype(dt)::value;
             uint32_t c[4];  // code pairs
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = v[j] & 0xFFFFu, hi = v[j] >> 16;
-                c[j] = e4m3_encode2(div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(lo) : to_f32<IN_F16>(lo)),
-                                    div(p.xdt == IN_BF16 ? to_f32<IN_BF16>(hi) : to_f32<IN_F16>(hi)));
-            }
+            for (int j = 0; j < 4; ++j) c[j] = enc2(to_f32<DT>(v[j] & 0xFFFFu), to_f32<DT>(v[j] >> 16));
             return u2{c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
         };
         // A is small here (at most 16 rows of a short K), so 32-bit indices
         const uint32_t slice = (uint32_t)(p.kt_per_split * TILE_K), k_lo = (uint32_t)(kt_begin * TILE_K);
         const uint32_t nv = (uint32_t)nvec, kk_ = (uint32_t)p.K, mm = (uint32_t)p.M;
-        auto cast_all = [&](auto div) {
+        auto cast_dt = [&](auto enc2, auto dt) {
+            auto codes = [&](const u4& v) { return codes8(v, enc2, dt); };
             if (whole) {
                 // slice = [0, KT*128): cast the K real columns, zero the padding
                 const uint32_t vpr = kk_ / 8;  // vectors per row
 #pragma unroll
                 for (int h = 0; h < HOLD; ++h) {
                     const uint32_t i = threadIdx.x + (uint32_t)h * T;
-                    if (i < nv) *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(held[h], div);
+                    if (i < nv) *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes(held[h]);
                 }
                 for (uint32_t i = threadIdx.x + (uint32_t)HOLD * T; i < nv; i += T)
-                    *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes8(((const u4*)x)[i], div);
+                    *(u2*)(aq_lds + (i / vpr) * slice + (i % vpr) * 8) = codes(((const u4*)x)[i]);
                 const uint32_t pad = (slice - kk_) / 8;  // zero 8-byte items past K in each row
                 for (uint32_t i = threadIdx.x; i < mm * pad; i += T)
                     *(u2*)(aq_lds + (i / pad) * slice + kk_ + (i % pad) * 8) = u2{0, 0};
@@ -256,20 +256,24 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(gemv
                 const uint32_t items = mm * slice / 8;
                 for (uint32_t i = threadIdx.x; i < items; i += T) {
                     const uint32_t m = i / (slice / 8), kk = (i % (slice / 8)) * 8, k = k_lo + kk;
-                    const u2 c = k < kk_ ? codes8(*(const u4*)(x + (size_t)m * kk_ + k), div) : u2{0, 0};
+                    const u2 c = k < kk_ ? codes(*(const u4*)(x + (size_t)m * kk_ + k)) : u2{0, 0};
                     *(u2*)(aq_lds + m * slice + kk) = c;
                 }
             }
         };
+        auto cast_all = [&](auto enc2) {
+            if (p.xdt == IN_BF16) cast_dt(enc2, DtTag<IN_BF16>{});
+            else cast_dt(enc2, DtTag<IN_F16>{});
+        };
         if (given) {
             const double inv = 1.0 / (double)sa;
-            cast_all([&](float v) { return quot_f32(v, inv); });
+            cast_all([&](float a, float b) { return e4m3_encode2(quot_f32(a, inv), quot_f32(b, inv)); });
         } else {
             const float y = 1.0f / sa;
             if (recip_div_ok(sa))
-                cast_all([&](float v) { return div_by_scale(v, sa, y); });
+                cast_all([&](float a, float b) { return e4m3_div2_finite(a, b, sa, y); });
             else
-                cast_all([&](float v) { return v / sa; });
+                cast_all([&](float a, float b) { return e4m3_encode2(a / sa, b / sa); });
         }
         __syncthreads();
     } else if constexpr (V == V_FP8 || V == V_FP8X) {

@@ -105,29 +105,29 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
     const int64_t nvec = numel / 8;
     const u4* xv = (const u4*)x;
     u2* qv = (u2*)xq;
-    auto body = [&](auto div) {
+    // enc2(a, b): the code pair of a / s and b / s
+    auto body = [&](auto enc2) {
         for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
              i += (int64_t)gridDim.x * QT) {
             u4 v = __builtin_nontemporal_load(&xv[i]);
             uint32_t c[4];  // code pairs
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                c[j] = e4m3_encode2(div(to_f32<DT>(v[j] & 0xFFFFu)), div(to_f32<DT>(v[j] >> 16)));
+            for (int j = 0; j < 4; ++j) c[j] = enc2(to_f32<DT>(v[j] & 0xFFFFu), to_f32<DT>(v[j] >> 16));
             u2 o = {c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
             __builtin_nontemporal_store(o, &qv[i]);
         }
         if (blockIdx.x == 0) {
             int64_t t = nvec * 8 + threadIdx.x;
-            if (t < numel) xq[t] = (uint8_t)e4m3_encode(div(to_f32<DT>(x[t])));
+            if (t < numel) xq[t] = (uint8_t)(enc2(to_f32<DT>(x[t]), 0.0f) & 0xFFu);
         }
     };
     // a given (static) scale is any float: only the dynamic scale amax/448
     // takes the reciprocal form
     const float y = 1.0f / s;
     if (SCALE_FROM == 0 && recip_div_ok(s))
-        body([&](float v) { return div_by_scale(v, s, y); });
+        body([&](float a, float b) { return e4m3_div2_finite(a, b, s, y); });
     else
-        body([&](float v) { return v / s; });
+        body([&](float a, float b) { return e4m3_encode2(a / s, b / s); });
 }
 
 // ------------------------------------------------ packed 8-bit activations
@@ -160,11 +160,12 @@ __device__ __forceinline__ void load_tile_in(const uint16_t* __restrict__ x, int
     }
 }
 
-// Codes of one tile's inputs, stored at tile t + 16 l (k .. k+15) and
-// tile t + 1024 + 16 l (k+16 .. k+31).  Zero inputs give zero codes.
-template <int DT, class Div>
+// Codes of one tile's inputs (enc2(a, b): the code pair of a / s and b / s),
+// stored at tile t + 16 l (k .. k+15) and tile t + 1024 + 16 l (k+16 ..
+// k+31).  Zero inputs give zero codes.
+template <int DT, class Enc>
 __device__ __forceinline__ void store_tile_codes(const TileIn& in, uint8_t* __restrict__ xq,
-                                                 int64_t t, int lane, Div div) {
+                                                 int64_t t, int lane, Enc enc2) {
     u4 out[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -173,8 +174,8 @@ __device__ __forceinline__ void store_tile_codes(const TileIn& in, uint8_t* __re
         for (int j = 0; j < 4; ++j) {
             const u4& v0 = in.v[h][0];
             const u4& v1 = in.v[h][1];
-            c[j] = e4m3_encode2(div(to_f32<DT>(v0[j] & 0xFFFFu)), div(to_f32<DT>(v0[j] >> 16)));
-            c[4 + j] = e4m3_encode2(div(to_f32<DT>(v1[j] & 0xFFFFu)), div(to_f32<DT>(v1[j] >> 16)));
+            c[j] = enc2(to_f32<DT>(v0[j] & 0xFFFFu), to_f32<DT>(v0[j] >> 16));
+            c[4 + j] = enc2(to_f32<DT>(v1[j] & 0xFFFFu), to_f32<DT>(v1[j] >> 16));
         }
         out[h] = u4{c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
     }
@@ -183,22 +184,23 @@ __device__ __forceinline__ void store_tile_codes(const TileIn& in, uint8_t* __re
     *(u4*)(tile + 1024) = out[1];
 }
 
-// The tile loop of the packed casts, for a given x -> x/s: wave w of block b
-// takes tiles t0 = b * WPB + w, t0 + gridDim.x * WPB, ...; the inputs of t0
-// were requested by the caller before it had the scale (`first`).
-template <int DT, class Div>
+// The tile loop of the packed casts, for a given encoder enc2(a, b) of the
+// code pair of a / s and b / s: wave w of block b takes tiles t0 = b * WPB +
+// w, t0 + gridDim.x * WPB, ...; the inputs of t0 were requested by the
+// caller before it had the scale (`first`).
+template <int DT, class Enc>
 __device__ __forceinline__ void cast_packed_tiles(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                   int64_t KT, uint8_t* __restrict__ xq, int64_t tiles,
-                                                  int lane, int r, int g, const TileIn& first, Div div) {
+                                                  int lane, int r, int g, const TileIn& first, Enc enc2) {
     constexpr int WPB = QT / 64;
     const int64_t stride = (int64_t)gridDim.x * WPB;
     int64_t t = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
     if (t >= tiles) return;
-    store_tile_codes<DT>(first, xq, t, lane, div);
+    store_tile_codes<DT>(first, xq, t, lane, enc2);
     for (t += stride; t < tiles; t += stride) {
         TileIn in;
         load_tile_in(x, M, K, KT, t, r, g, in);
-        store_tile_codes<DT>(in, xq, t, lane, div);
+        store_tile_codes<DT>(in, xq, t, lane, enc2);
     }
 }
 
@@ -240,10 +242,10 @@ __global__ __launch_bounds__(QT) void cast_e4m3_packed_kernel(const uint16_t* __
     const float y = 1.0f / s;
     if (recip_div_ok(s))
         cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, first,
-                              [&](float v) { return div_by_scale(v, s, y); });
+                              [&](float a, float b) { return e4m3_div2_finite(a, b, s, y); });
     else
         cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, first,
-                              [&](float v) { return v / s; });
+                              [&](float a, float b) { return e4m3_encode2(a / s, b / s); });
 }
 
 // Static-scale cast into the packed layout: s is given (checkpoint
@@ -260,8 +262,9 @@ __global__ __launch_bounds__(QT) void cast_e4m3_packed_static_kernel(const uint1
     TileIn first;
     load_tile_in(x, M, K, KT, t0 < tiles ? t0 : 0, r, g, first);
     const double inv = 1.0 / (double)*given;
-    cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, first,
-                          [&](float v) { return quot_f32(v, inv); });
+    cast_packed_tiles<DT>(x, M, K, KT, xq, tiles, lane, r, g, first, [&](float a, float b) {
+        return e4m3_encode2(quot_f32(a, inv), quot_f32(b, inv));
+    });
 }
 
 // Row-major 8-bit codes [M, K] -> packed layout: one wave per 16 x 128
