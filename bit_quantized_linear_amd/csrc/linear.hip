@@ -1098,17 +1098,37 @@ struct GemvPlan {
 };
 
 // Blocks of GEMV_WAVES waves stream one 16-channel strip each.  Few strips
-// (short N) would leave CUs idle, so K is split across blocks (with a
-// fixed-order reduce) until there are about 256 blocks, or 512 when K is
-// short (KT < 32), keeping at least 8 (4) k-tiles per split.
-static GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
+// (short N) leave CUs idle, so K may be split across blocks (with a
+// fixed-order reduce): up to about 256 blocks, or 512 when K is short
+// (KT < 32), keeping at least 8 (4) k-tiles per split.  Of those split
+// counts the plan takes the cheapest by a cost fitted to timings of M <= 16
+// fp8 linears on MI355X with N = 1024-2048: a block streams its strip's
+// weight bytes at about 45 GB/s after a fixed start (A comes from L2), and
+// a K split adds the reduce launch and the partial sums, about 3.6 us.
+// Short strips are therefore not split (M = 1, N = K = 2048: 9.3 -> 5.5 us;
+// M = 16, N = 1024, K = 8192: 15.5 -> 14.2 us), long ones are (M = 1,
+// N = 1024, K = 16384: four splits, 9.8 us against 10.5 unsplit).
+static GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int variant) {
     GemvPlan pl;
     pl.KT = (K + TILE_K - 1) / TILE_K;
     const int64_t groups = (N / TILE_N) * ((M + 15) / 16);
     const int64_t target = pl.KT < 32 ? 512 : 256, min_kt = pl.KT < 32 ? 4 : 8;
-    int s = 1;
+    int smax = 1;
     if (M <= SMALL_M)
-        while (groups * s < target && s * 2 <= MAX_SPLITS && pl.KT / (s * 2) >= min_kt) s *= 2;
+        while (groups * smax < target && smax * 2 <= MAX_SPLITS && pl.KT / (smax * 2) >= min_kt)
+            smax *= 2;
+    const bool int4 = variant == V_W4A8 || variant == V_W4A8G || variant == V_W4A16G;
+    const double strip_bytes = (double)pl.KT * (int4 ? INT4_TILE_BYTES : 2048);
+    constexpr double BLOCK_BYTES_PER_US = 45e3, SPLIT_US = 3.6;
+    int s = 1;
+    double best = strip_bytes / BLOCK_BYTES_PER_US;
+    for (int c = 2; c <= smax; c *= 2) {
+        const double cost = SPLIT_US + strip_bytes / c / BLOCK_BYTES_PER_US;
+        if (cost < best) {
+            best = cost;
+            s = c;
+        }
+    }
     pl.kt_per_split = (pl.KT + s - 1) / s;
     pl.splits = (int)((pl.KT + pl.kt_per_split - 1) / pl.kt_per_split);
     return pl;
@@ -1123,7 +1143,7 @@ size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
 
 size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant) {
     if (!use_small_m(variant, M, N, K) || M > SMALL_M) return 0;
-    GemvPlan pl = plan_gemv(M, N, K);
+    GemvPlan pl = plan_gemv(M, N, K, variant);
     return pl.splits > 1 ? (size_t)pl.splits * M * N * 4 : 0;
 }
 
@@ -1132,7 +1152,7 @@ size_t small_m_ws_bytes(int64_t M, int64_t N, int64_t K, int variant) {
 // M = 16, K = 1024 (two launches fewer), 45 % slower at M = 16, K = 4096.
 bool fused_small_m(int64_t M, int64_t N, int64_t K) {
     if (M > FUSED_M || (M > 4 && M * K > 16384)) return false;
-    GemvPlan pl = plan_gemv(M, N, K);
+    GemvPlan pl = plan_gemv(M, N, K, V_FP8X);
     return M * pl.kt_per_split * TILE_K <= FUSED_LDS;
 }
 
@@ -1362,7 +1382,7 @@ hipError_t launch_linear(const LinearArgs& args, void* ws, size_t ws_bytes, hipS
     p.a_rowmajor = args.a_rowmajor;
     p.given_scale = args.given_scale;
     if (use_small_m(args.variant, args.M, args.N, args.K)) {
-        GemvPlan pl = plan_gemv(args.M, args.N, args.K);
+        GemvPlan pl = plan_gemv(args.M, args.N, args.K, args.variant);
         p.KT = pl.KT;
         p.kt_per_split = pl.kt_per_split;
         p.splits = pl.splits;

@@ -45,7 +45,10 @@ def _replays_match(run, out, noise):
 @pytest.mark.parametrize("fast", [False, True])
 # (1024, 4096, 4096) and (300, 2048, 4096): the exact tile kernel with eight
 # waves, the latter with K split; (520, 4208, 8000): four waves, K split
+# (2, 256, 34816) and (16, 256, 17408): the small-M kernel with K split
+# eight ways, fused quantization and a separate cast
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (3, 1024, 1024), (16, 1024, 1024), (8, 4096, 4096),
+                                   (2, 256, 34816), (16, 256, 17408),
                                    (1024, 4096, 4096), (130, 272, 400), (300, 2048, 4096),
                                    (520, 4208, 8000)])
 def test_fp8_linear_graph(M, N, K, fast):

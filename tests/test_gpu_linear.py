@@ -213,11 +213,11 @@ def test_w4a8_ragged(M, N, K):
 
 @pytest.mark.parametrize("M", [1, 3, 5, 16])
 def test_small_m_split_k(M):
-    """N = 256, K = 4096: the small-M kernels split K four ways (8 k-tiles
-    per split, so half of a wave's weight batches lie past its split's range)
-    and add the partial sums in a fixed order; fp8 (fused quantization for
-    M <= 4), W8A16 and W4A8."""
-    N, K = 256, 4096
+    """N = 256, K = 34816: the small-M kernels split K eight ways (34 k-tiles
+    per split, so each wave's last weight batch lies partly past its split's
+    range) and add the partial sums in a fixed order; fp8 (fused quantization
+    for M <= 4), W8A16 and W4A8."""
+    N, K = 256, 34816
     _fp8_case(3, 12, M, N, K, "bf16", False, "channels", torch.bfloat16)
     g = wl.rng(9, N, K, 12)
     bits = wl.weight(g, N, K, "f16")
@@ -238,16 +238,16 @@ def test_small_m_split_k(M):
 
 
 def test_w8a16_split_k_infinite_activation():
-    """M = 1, N = 256, K = 4096 (K split four ways); one activation column,
-    in the third split's range, is +inf.  Each output is then +-inf by the
+    """M = 1, N = 256, K = 34816 (K split eight ways, 4352 columns each); one
+    activation column, in the third split's range, is +inf.  Each output is then +-inf by the
     sign of its weight code in that column, or NaN where that code is +-0,
     as the oracle's IEEE sums give.  A split that read the column outside
     its own range would multiply it by zero weight tiles and make every
     output NaN."""
-    N, K = 256, 4096
+    N, K = 256, 34816
     g = np.random.Generator(np.random.PCG64(77))
     wq = _random_codes(g, (N, K))
-    col = 2 * 1024 + 300
+    col = 2 * 4352 + 300
     wq[0:3, col] = [0x00, 0x80, 0x38]
     pw = bql.prepack_weight(dev(wq), "fp8_channel", scales=torch.ones(N, device=DEV))
     a = oracle.decode_input(wl.activation(wl.rng(9, 1, 13), 1, K, "f16"), "f16").astype(np.float32)

@@ -54,10 +54,11 @@ def test_w4a16_group_workload(M, KN):
 # (77, 300, 130), a column block with waves wholly past N (272), one and
 # two k-tiles (the pipeline's shortest runs), odd k-tile counts (384), and
 # few blocks with a long K, whose k range is split over blocks (fp32
-# partial sums, then the split-K reduce): (200, 1040, 4096), (1024, 4096, 4096)
+# partial sums, then the split-K reduce): (200, 1040, 4096), (1024, 4096, 4096);
+# (8, 256, 65536): the small-M kernel with K split eight ways
 @pytest.mark.parametrize("M,N,K", [(77, 1040, 384), (3, 16, 128), (300, 272, 1280), (16, 2064, 4096),
                                    (1, 4096, 14336), (40, 512, 128), (130, 4096, 256), (17, 784, 640),
-                                   (200, 1040, 4096), (1024, 4096, 4096)])
+                                   (200, 1040, 4096), (1024, 4096, 4096), (8, 256, 65536)])
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16, torch.float32])
 def test_w4a16_group_ragged(M, N, K, out):
     g = wl.rng(94, M, N, K)
