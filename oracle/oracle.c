@@ -37,8 +37,10 @@
  *
  * Readings where the pages are silent are ours and are listed in the design
  * notes: RNE, saturation to +-448, sign kept on zero/underflow, IEEE fp32
- * division x / scale, scale = 1 when amax = 0, int8 per-token scale =
- * amax / 127 with RNE and clamp to +-127, low nibble = even k for logical int4.
+ * division x / scale, scale = 1 when amax = 0, a NaN in the tensor (row)
+ * makes its E4M3 amax and scale NaN, int8 per-token scale = amax / 127 with
+ * RNE and clamp to +-127 (NaN inputs outside its contract), low nibble =
+ * even k for logical int4.
  *
  * Style: plain loops, no blocking, no reordering beyond the definitions.
  * OpenMP only splits independent output rows across host cores.
@@ -145,12 +147,21 @@ static float scale_from_amax(float amax, float qmax) {
     return amax / qmax;
 }
 
+/* max |x| over n values.  A NaN anywhere makes it NaN, as the maximum of a
+ * torch tensor holding a NaN is NaN; the scale is then NaN and so is every
+ * code of that tensor (row). */
+static float amax_of(const float* x, int64_t n) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        if (isnan(x[i])) return NAN;
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+    }
+    return amax;
+}
+
 /* Dynamic per-tensor quantization of n fp32 values. */
 void bqo_quant_per_tensor(const float* x, int64_t n, uint8_t* q, float* scale_out) {
-    float amax = 0.0f;
-    for (int64_t i = 0; i < n; ++i)
-        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
-    float s = scale_from_amax(amax, 448.0f);
+    float s = scale_from_amax(amax_of(x, n), 448.0f);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         float r = x[i] / s;                     /* IEEE fp32 division */
@@ -165,10 +176,7 @@ void bqo_quant_per_row(const float* x, int64_t rows, int64_t cols, uint8_t* q,
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         const float* xr = x + r * cols;
-        float amax = 0.0f;
-        for (int64_t k = 0; k < cols; ++k)
-            if (fabsf(xr[k]) > amax) amax = fabsf(xr[k]);
-        float s = scale_from_amax(amax, 448.0f);
+        float s = scale_from_amax(amax_of(xr, cols), 448.0f);
         for (int64_t k = 0; k < cols; ++k)
             q[r * cols + k] = bqo_e4m3_encode((double)(xr[k] / s));
         scales[r] = s;

@@ -214,6 +214,38 @@ def test_quant_codes_are_nearest_to_scaled_input():
         assert abs(tab[qi] - r) == best
 
 
+def test_quant_nonfinite_amax_follows_torch():
+    # the amax of a tensor holding a NaN is NaN and of one holding an
+    # infinity is infinite, as torch computes it; the scale amax / 448 is
+    # then NaN (every code the NaN code) or infinite (every finite x / s a
+    # zero of x's sign, inf / inf the NaN code)
+    x = _sample(6)
+    y = x.copy()
+    y[1, 7] = np.nan
+    assert torch.isnan(torch.from_numpy(y).abs().max())
+    q, s = oracle.quant_per_tensor(y)
+    assert np.isnan(s) and np.all((q & 0x7F) == 0x7F)
+    y = x.copy()
+    y[2, 3] = -np.inf
+    assert torch.isinf(torch.from_numpy(y).abs().max())
+    q, s = oracle.quant_per_tensor(y)
+    assert np.isposinf(s)
+    fin = np.isfinite(y)
+    assert np.array_equal(q[fin], np.where(np.signbit(y[fin]), 0x80, 0x00))
+    assert (q[2, 3] & 0x7F) == 0x7F
+    # per row: only the row holding the NaN is NaN; the others are
+    # quantized as they are alone
+    y = x.copy()
+    y[3, 0] = np.nan
+    q, s = oracle.quant_per_row(y)
+    for n in range(y.shape[0]):
+        if n == 3:
+            assert np.isnan(s[n]) and np.all((q[n] & 0x7F) == 0x7F)
+        else:
+            qn, sn = oracle.quant_per_tensor(y[n])
+            assert np.array_equal(q[n], qn) and s[n] == sn, n
+
+
 def test_per_row_with_equal_rows_equals_per_tensor():
     x = _sample(5)
     amax = np.abs(x).max()
