@@ -277,6 +277,29 @@ def test_w4a8_extreme_values_exact():
         assert np.array_equal(host(acc).astype(np.int64), oracle.w4a8_acc(aq[:m], w))
 
 
+@pytest.mark.parametrize("M,K", [(2, 1024), (16, 1024), (16, 4096)])
+@pytest.mark.parametrize("kind", ["nan", "inf"])
+def test_small_m_nonfinite_activation(kind, M, K):
+    """A NaN or an infinity in A at small M (fused quantization at M = 2 and
+    M = 16, K = 1024; the amax pass and cast at M = 16, K = 4096): the
+    scale is NaN or infinite as the oracle's, and the infinity's or NaN's
+    code (NaN) makes every output NaN, as the oracle's IEEE sums give."""
+    N = 1024
+    g = wl.rng(13, M, K)
+    a = oracle.decode_input(wl.activation(g, M, K, "bf16", "channels"), "bf16").astype(np.float32)
+    a[M // 2, K // 3] = np.nan if kind == "nan" else np.inf
+    bits = wl.to_bits(a, "bf16")
+    pw = bql.prepack_weight(dev16(wl.weight(g, N, K, "bf16"), "bf16"), "fp8_tensor")
+    sa = torch.empty(1, dtype=torch.float32, device=DEV)
+    y = bql.fp8_linear(dev16(bits, "bf16"), pw, a_scale=sa, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore"):
+        _, s_ref = oracle.quant_per_tensor(oracle.decode_input(bits, "bf16"))
+    got = host(sa)[0]
+    assert (np.isnan(got) and np.isnan(s_ref)) or got == s_ref
+    assert np.isnan(host_f64(y)).all()
+
+
 def test_m_zero_is_a_no_op():
     W = _weights(1, 0, 1024, 1024, "f16", False)
     pw = _packed(1, 0, 1024, 1024, "f16", False)

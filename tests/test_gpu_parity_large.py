@@ -60,6 +60,32 @@ def _unpack_activation_tiles(buf: np.ndarray, M: int, K: int) -> np.ndarray:
     return logical[:M, :K]
 
 
+def _check_in_linear_codes(a_bits, dtype, M, N, K, wbits, nan_sign_free=False):
+    """The scale and the packed codes of a bql_fp8_linear call's in-linear
+    quantizer equal the oracle's; with nan_sign_free, a NaN code may carry
+    either sign (the sign of a NaN made by a division is not fixed by IEEE
+    754), every other code must be identical."""
+    pw = bql.prepack_weight(dev16(wbits, "bf16"), "fp8_tensor")
+    ws = torch.zeros(bql.fp8_linear_workspace_size(M, N, K), dtype=torch.uint8, device=DEV)
+    sa = torch.empty(1, dtype=torch.float32, device=DEV)
+    bql.fp8_linear(dev16(a_bits, dtype), pw, a_scale=sa, ws=ws)
+    torch.cuda.synchronize()
+    wsb = host(ws)
+    scale_in_ws = wsb[4096:4100].view(np.float32)[0]
+    got = _unpack_activation_tiles(wsb[8192:], M, K)
+    with np.errstate(invalid="ignore"):
+        aq, sa_ref = oracle.quant_per_tensor(oracle.decode_input(a_bits, dtype))
+    same_scale = (lambda x, y: x.view(np.uint32) == y.view(np.uint32) or (np.isnan(x) and np.isnan(y)))
+    assert same_scale(host(sa)[0], np.float32(sa_ref))
+    assert same_scale(np.float32(scale_in_ws), np.float32(sa_ref))
+    if nan_sign_free:
+        nan = (aq & 0x7F) == 0x7F
+        assert np.array_equal((got & 0x7F) == 0x7F, nan), "NaN codes differ"
+        got, aq = got[~nan], aq[~nan]
+    assert np.array_equal(got, aq), f"{int((got != aq).sum())} codes differ"
+    return aq
+
+
 @pytest.mark.parametrize("M,N,K", [(1024, 4096, 14336), (4096, 8192, 28672)])
 def test_in_linear_activation_codes(M, N, K):
     # the quantizer's codes as the tile kernels read them, read back from
@@ -68,19 +94,37 @@ def test_in_linear_activation_codes(M, N, K):
     cfg, idx = (3, 3) if K == 14336 else (4, 3)
     a_bits = wl.activation(wl.rng(cfg, idx, M, 3), M, K, "bf16", "channels")
     wbits = wl.weight(wl.rng(cfg, idx, 1), N, K, "bf16")
-    pw = bql.prepack_weight(dev16(wbits, "bf16"), "fp8_tensor")
-    ws = torch.zeros(bql.fp8_linear_workspace_size(M, N, K), dtype=torch.uint8, device=DEV)
-    sa = torch.empty(1, dtype=torch.float32, device=DEV)
-    bql.fp8_linear(dev16(a_bits, "bf16"), pw, a_scale=sa, ws=ws)
-    torch.cuda.synchronize()
-    wsb = host(ws)
-    scale_in_ws = wsb[4096:4100].view(np.float32)[0]
-    got = _unpack_activation_tiles(wsb[8192:], M, K)
-    aq, sa_ref = oracle.quant_per_tensor(oracle.decode_input(a_bits, "bf16"))
-    assert host(sa)[0].view(np.uint32) == np.float32(sa_ref).view(np.uint32)
-    assert np.float32(scale_in_ws).view(np.uint32) == np.float32(sa_ref).view(np.uint32)
-    assert np.array_equal(got, aq), f"{int((got != aq).sum())} codes differ"
+    aq = _check_in_linear_codes(a_bits, "bf16", M, N, K, wbits)
     say(f"  {M * K} codes identical, saturated {np.mean((aq & 0x7F) == 0x7E):.2e}")
+
+
+# Small activations: the small-M kernel's packed input (16, 4096) and
+# (24, 2048) in fp16, the tile kernels' at a ragged row strip and k-tile
+# (40, 6544) and (65, 4096).
+@pytest.mark.parametrize("M,N,K,dtype", [(16, 1024, 4096, "bf16"), (24, 1040, 2048, "f16"),
+                                         (40, 1040, 6544, "bf16"), (65, 1024, 4096, "bf16")])
+def test_in_linear_activation_codes_small(M, N, K, dtype):
+    g = wl.rng(97, M, K)
+    a_bits = wl.activation(g, M, K, dtype, "channels")
+    _check_in_linear_codes(a_bits, dtype, M, N, K, wl.weight(g, N, K, "bf16"))
+
+
+@pytest.mark.parametrize("M,K", [(16, 2048), (80, 4096)])
+@pytest.mark.parametrize("kind", ["zeros", "inf", "nan"])
+def test_in_linear_activation_codes_special(kind, M, K):
+    # a zero tensor (scale 1, zero codes), an infinity (infinite scale: codes
+    # of x / inf, NaN for the infinity itself) and a NaN (NaN scale: NaN
+    # codes) through the in-linear quantizer of the small-M kernel (16 x
+    # 2048) and of the tile kernels (80 x 4096)
+    N = 1024
+    g = wl.rng(98, M, K)
+    a = oracle.decode_input(wl.activation(g, M, K, "bf16", "channels"), "bf16").astype(np.float32)
+    if kind == "zeros":
+        a[:] = 0.0
+    else:
+        a[5, 777] = np.inf if kind == "inf" else np.nan
+    _check_in_linear_codes(wl.to_bits(a, "bf16"), "bf16", M, N, K, wl.weight(g, N, K, "bf16"),
+                           nan_sign_free=True)
 
 
 def test_unpack_helper_layout():

@@ -130,3 +130,27 @@ def test_int8_worked_rows():
     assert list(host(s)) == [1.0, 2.0]
     assert list(host(q)[0][:4]) == [127, -64, 0, 2]
     assert list(host(q)[1][:4]) == [-127, 0, 2, 2]
+
+
+@pytest.mark.parametrize("n", [4096, 1000005])
+@pytest.mark.parametrize("kind", ["nan", "inf"])
+def test_dynamic_nonfinite_tensor(n, kind):
+    """A NaN anywhere makes the amax, the scale and every code NaN; an
+    infinity makes the scale infinite, every finite value a zero code of its
+    sign and the infinity itself the NaN code.  The sign of a NaN made by a
+    division is not fixed by IEEE 754, so NaN codes may carry either sign."""
+    g = wl.rng(10, n)
+    x = oracle.decode_input(wl.activation(g, 1, n, "bf16", "channels"), "bf16").ravel().astype(np.float32)
+    x[n // 3] = np.nan if kind == "nan" else np.inf
+    bits = wl.to_bits(x, "bf16")
+    xq, s = bql.quantize_dynamic(dev16(bits, "bf16"))
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore"):
+        q_ref, s_ref = oracle.quant_per_tensor(oracle.decode_input(bits, "bf16"))
+    got_s = host(s)[0]
+    assert (np.isnan(got_s) and np.isnan(s_ref)) or got_s == s_ref
+    got = host(xq)
+    nan = (q_ref & 0x7F) == 0x7F
+    assert np.array_equal((got & 0x7F) == 0x7F, nan)
+    assert np.array_equal(got[~nan], q_ref[~nan])
+
