@@ -38,6 +38,30 @@ def test_prepack_fp8_computed_scales(fmt, dtype, N, K):
     assert pw.packed.numel() == bql.packed_weight_bytes(N, K, fmt)
 
 
+@pytest.mark.parametrize("fmt", ["fp8_tensor", "fp8_channel"])
+def test_prepack_fp8_nan_weight(fmt):
+    # a NaN weight makes the amax of its tensor (per tensor) or of its row
+    # (per channel) NaN: that scale is NaN and its codes are NaN codes, of
+    # either sign (a division's NaN has no fixed sign); the other rows keep
+    # their exact codes and scales
+    N, K = 160, 272
+    g = wl.rng(7, N, K, 1)
+    w = oracle.decode_input(wl.weight(g, N, K, "bf16"), "bf16").astype(np.float32)
+    w[37, 100] = np.nan
+    bits = wl.to_bits(w, "bf16")
+    pw = bql.prepack_weight(dev16(bits, "bf16"), fmt)
+    codes = host(bql.unpack_weight(pw))
+    wf = oracle.decode_input(bits, "bf16")
+    q, s = oracle.quant_per_tensor(wf) if fmt == "fp8_tensor" else oracle.quant_per_row(wf)
+    s = np.atleast_1d(np.asarray(s, dtype=np.float32))
+    got_s = host(pw.scales)
+    assert np.array_equal(np.isnan(got_s), np.isnan(s))
+    assert np.array_equal(got_s[~np.isnan(s)].view(np.uint32), s[~np.isnan(s)].view(np.uint32))
+    nan = (q & 0x7F) == 0x7F
+    assert nan.any() and np.array_equal((codes & 0x7F) == 0x7F, nan)
+    assert np.array_equal(codes[~nan], q[~nan])
+
+
 def test_prepack_given_fp16_channel_scales_w8a16_workload():
     N = K = 4096
     g = wl.rng(2, 0)
