@@ -96,7 +96,9 @@ __device__ __forceinline__ void store_rows_t(const LinParams& p, void* dst, int6
     static_assert(!RAW || OUT == OUT_F32, "partials are fp32");
     constexpr int ESZ = OUT == OUT_E4M3 ? 1 : (OUT == OUT_F32 ? 4 : 2);
     constexpr int PER = 16 / ESZ, CHUNKS = FN * 16 / PER, ITEMS = ROWS * CHUNKS, ITERS = (ITEMS + 63) / 64;
-    const float os = OUT == OUT_E4M3 ? *p.ep.out_scale : 1.0f;
+    // E4M3 output: y / output_scale as the IEEE quotient (quot_f32, from the
+    // fp64 reciprocal), two codes per conversion instruction
+    const double inv = OUT == OUT_E4M3 ? 1.0 / (double)*p.ep.out_scale : 1.0;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int q = lane + 64 * it;
@@ -115,13 +117,16 @@ __device__ __forceinline__ void store_rows_t(const LinParams& p, void* dst, int6
         if constexpr (OUT == OUT_BF16) {
 #pragma unroll
             for (int e = 0; e < PER; e += 2) w[e / 2] = f32x2_to_bf16x2(y[e], y[e + 1]);
+        } else if constexpr (OUT == OUT_E4M3) {
+#pragma unroll
+            for (int e = 0; e < PER; e += 2)
+                w[e / 4] |= e4m3_encode2(quot_f32(y[e], inv), quot_f32(y[e + 1], inv)) << (8 * (e % 4));
         } else {
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
                 uint32_t b;
                 if constexpr (OUT == OUT_F32) b = __float_as_uint(y[e]);
-                else if constexpr (OUT == OUT_F16) b = f32_to_f16_bits(y[e]);
-                else b = e4m3_encode(y[e] / os);
+                else b = f32_to_f16_bits(y[e]);
                 w[e * ESZ / 4] |= b << (8 * ((e * ESZ) % 4));
             }
         }

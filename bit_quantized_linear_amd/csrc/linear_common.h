@@ -180,7 +180,7 @@ __device__ __forceinline__ uint32_t out_bits(const Epilogue& ep, float sa, int64
     if (ep.ydt == OUT_F16) return f32_to_f16_bits(y);
     if (ep.ydt == OUT_BF16) return f32_to_bf16_bits(y);
     if (ep.ydt == OUT_F32) return __float_as_uint(y);
-    return e4m3_encode(y / *ep.out_scale);
+    return e4m3_encode2(y / *ep.out_scale, 0.0f) & 0xFFu;
 }
 
 __device__ __forceinline__ int out_size(int ydt) {
