@@ -178,7 +178,9 @@ def test_cfg5_w4a8(idx, M):
 
 # ---------------------------------------------------------- edge cases
 
-@pytest.mark.parametrize("M", [1, 3, 16, 17, 130, 300])
+# M = 16 / 17: the small-M kernel / the tile kernels; 128 / 129: the
+# k-split kernel / the exact 256-row kernel
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 128, 129, 130, 300])
 @pytest.mark.parametrize("N,K", [(48, 144), (16, 16), (272, 400)])
 def test_fp8_ragged(M, N, K):
     _fp8_case(8, N * 1000 + K, M, N, K, "bf16", True, "entries", torch.bfloat16, rows_count=400)
