@@ -7,10 +7,11 @@
 // with one fused multiply-add by the group scale.
 //
 // Organisation (gfx950: 4 SIMDs per CU, 160 KiB LDS per CU):
-//   * A block computes a 128 x 256 output tile with four waves side by side
-//     in N, one per SIMD; each wave owns all 128 rows and 64 channels: 32
-//     output tiles of 16 x 16 whose fp32 accumulators stay in ordinary vector
-//     registers, because the per-group fold is vector-ALU work.  The int4
+//   * A block computes a 128 x 256 (or, where that fills the CUs better,
+//     128 x 128) output tile with four waves side by side in N, one per SIMD;
+//     each wave owns all 128 rows and 64 (32) channels: 32 (16) output tiles
+//     of 16 x 16 whose fp32 accumulators stay in ordinary vector registers,
+//     because the per-group fold is vector-ALU work.  The int4
 //     decode (about 44 vector instructions per 16-channel x 128-k weight
 //     tile) is paid once per 8 row strips, and the fold once per 4 MFMAs.
 //   * A (row-major fp16 in HBM) reaches LDS by LDS-DMA (buffer_load ... lds),
@@ -28,7 +29,7 @@
 //     strips stay in registers for the whole k-tile; in the last strip pass
 //     every A strip is replaced by the next k-tile's right after its last use.
 //   * Output tiles go to the 8 XCDs in contiguous ranges; the epilogue stages
-//     the wave's 128 x 64 tile in LDS and writes it with 16-byte stores.
+//     the wave's 128-row tile in LDS and writes it with 16-byte stores.
 #include <atomic>
 #include <type_traits>
 
@@ -41,27 +42,32 @@ namespace {
 constexpr int QM = 128;                    // block rows
 constexpr int QW = 4;                      // waves per block, side by side in N
 constexpr int QFM = QM / 16;               // 16-row strips per wave (8)
-constexpr int QFN = 4;                     // 16-channel strips per wave
-constexpr int QN = QW * QFN * 16;          // block columns (256)
 constexpr int QSTAGE = QM * 256;           // one k-tile of A: 32 KiB
 constexpr int QS = 4;                      // LDS ring depth
 constexpr int QLDS = QS * QSTAGE;          // 128 KiB
 constexpr int QLD = QFM;                   // A DMA instructions per wave per stage
-constexpr int QEPI_ROW = QFN * 16 * 4 + 16;      // staged row: up to 64 fp32, padded
-constexpr int QEPI_WAVE = QM * QEPI_ROW;
-constexpr int QLDS_ALL = QLDS > QW * QEPI_WAVE ? QLDS : QW * QEPI_WAVE;
-static_assert(QLDS_ALL <= 160 * 1024, "LDS");
-static_assert(QLD + 2 * QFN < 64, "vmcnt range");
+
+// Block geometry for QFN 16-channel strips per wave (4: 128 x 256 blocks,
+// 2: 128 x 128).
+template <int QFN>
+struct QCfg {
+    static constexpr int QN = QW * QFN * 16;              // block columns
+    static constexpr int EPI_ROW = QFN * 16 * 4 + 16;     // staged row: up to 16 QFN fp32, padded
+    static constexpr int EPI_WAVE = QM * EPI_ROW;
+    static constexpr int LDS_ALL = QLDS > QW * EPI_WAVE ? QLDS : QW * EPI_WAVE;
+    static_assert(LDS_ALL <= 160 * 1024, "LDS");
+    static_assert(QLD + 2 * QFN < 64, "vmcnt range");
+};
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Writes the wave's staged 128 x 64 tile (OUT bits, QEPI_ROW bytes per row)
-// to y (row stride ldy elements) with 16-byte stores.  N is a multiple of 16, so a store's columns
-// lie all inside or all outside N.
-template <int OUT>
+// Writes the wave's staged 128 x 16 QFN tile (OUT bits, EPI_ROW bytes per
+// row) to y (row stride ldy elements) with 16-byte stores.  N is a multiple
+// of 16, so a store's columns lie all inside or all outside N.
+template <int OUT, int QFN>
 __device__ __forceinline__ void copy_out(const LinParams& p, uint8_t* y, int64_t ldy, const uint8_t* band,
                                          int64_t m0, int64_t col0, int lane) {
-    constexpr int ESZ = OUT == OUT_F32 ? 4 : 2;
+    constexpr int ESZ = OUT == OUT_F32 ? 4 : 2, QEPI_ROW = QCfg<QFN>::EPI_ROW;
     constexpr int CHUNKS = QFN * 16 * ESZ / 16, ITERS = QM * CHUNKS / 64;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -106,8 +112,10 @@ __device__ __forceinline__ void step_order(bool reads) {
 
 }  // namespace
 
+template <int QFN>
 __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_w4a16_kernel(LinParams p) {
+    constexpr int QN = QCfg<QFN>::QN, QEPI_ROW = QCfg<QFN>::EPI_ROW, QEPI_WAVE = QCfg<QFN>::EPI_WAVE;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // the wave index and the tile coordinates (whose 64-bit divisions run on
     // the vector ALU) are uniform: read them as such, so that the buffer
@@ -291,7 +299,7 @@ void gemm_w4a16_kernel(LinParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[QFM - 1][QFN - 1][r] = __builtin_fmaf(tl[r], sl, acc[QFM - 1][QFN - 1][r]);
 
-    // ---- epilogue: convert, stage the wave's 128 x 64 tile in LDS, write
+    // ---- epilogue: convert, stage the wave's 128 x 16 QFN tile in LDS, write
     wait_vmcnt<0>();
     compiler_fence();
     __syncthreads();
@@ -313,9 +321,9 @@ void gemm_w4a16_kernel(LinParams p) {
                 }
         __builtin_amdgcn_wave_barrier();
         if (p.splits > 1)  // fp32 partial sums of this split, summed by the split-K reduce
-            copy_out<OUT>(p, (uint8_t*)p.partial + (int64_t)blockIdx.y * p.M * p.N * 4, p.N, band, m0, col0, lane);
+            copy_out<OUT, QFN>(p, (uint8_t*)p.partial + (int64_t)blockIdx.y * p.M * p.N * 4, p.N, band, m0, col0, lane);
         else
-            copy_out<OUT>(p, (uint8_t*)p.ep.y, p.ep.ldy, band, m0, col0, lane);
+            copy_out<OUT, QFN>(p, (uint8_t*)p.ep.y, p.ep.ldy, band, m0, col0, lane);
     };
     if (p.splits > 1) {
         epilogue(std::integral_constant<int, OUT_F32>{});
@@ -334,7 +342,9 @@ bool w4a16_tile_fits(int64_t M, int64_t N, int64_t K) {
     return K <= (int64_t(1) << 22);
 }
 
-hipError_t launch_gemm_w4a16(const LinParams& p, hipStream_t stream) {
+template <int QFN>
+static hipError_t launch_fn(const LinParams& p, hipStream_t stream) {
+    using C = QCfg<QFN>;
     // dynamic LDS above 64 KiB needs the attribute, set once per device
     // (before any graph capture: the first launch is eager)
     static std::atomic<uint64_t> configured{0};
@@ -343,37 +353,51 @@ hipError_t launch_gemm_w4a16(const LinParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const uint64_t bit = uint64_t(1) << (dev & 63);
     if (!(configured.load(std::memory_order_acquire) & bit)) {
-        e = hipFuncSetAttribute((const void*)gemm_w4a16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                QLDS_ALL);
+        e = hipFuncSetAttribute((const void*)gemm_w4a16_kernel<QFN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                C::LDS_ALL);
         if (e != hipSuccess) return e;
         configured.fetch_or(bit, std::memory_order_acq_rel);
     }
-    const int64_t blocks = ((p.M + QM - 1) / QM) * ((p.N + QN - 1) / QN);
-    gemm_w4a16_kernel<<<dim3((unsigned)blocks, (unsigned)p.splits), 64 * QW, QLDS_ALL, stream>>>(p);
+    const int64_t blocks = ((p.M + QM - 1) / QM) * ((p.N + C::QN - 1) / C::QN);
+    gemm_w4a16_kernel<QFN><<<dim3((unsigned)blocks, (unsigned)p.splits), 64 * QW, C::LDS_ALL, stream>>>(p);
     return hipGetLastError();
 }
 
-int w4a16_tile_splits(int64_t M, int64_t N, int64_t K) {
-    // One block per CU at a time: a launch of s splits takes
-    // ceil(blocks * s / CUs) rounds of ceil(KT / s) k-tiles.  The fp32
-    // partial sums are written and read back once each (8 bytes per output
-    // and split); measured, one k-tile of a block takes about as long as the
-    // chip moves 9 MB.  The split count minimizes the sum, in k-tile times,
-    // keeping 4+ k-tiles per split.
+// Block width and K splits for a shape.  One block per CU at a time, so a
+// launch of s splits takes ceil(blocks * s / CUs) rounds of ceil(KT / s)
+// k-tiles.  A k-tile of a 128 x 128 block costs 0.6 of a 128 x 256 block's
+// (the same A stage, half the weight decode and MFMAs); the fp32 partial
+// sums are written and read back once each (8 bytes per output and split),
+// and a 128 x 256 block's k-tile takes about as long as the chip moves 9 MB.
+// Measured at M = 256 .. 1024 and K = N = 4096 .. 8192 the model picks the
+// faster width at every shape or one within 2 % of it (128 x 128 blocks:
+// 9-11 % faster at K = N = 4096 and at M = 256, K = N = 5120; up to 32 %
+// slower where they need a second round).  At most 8 splits of 4+ k-tiles.
+W4A16Plan w4a16_plan(int64_t M, int64_t N, int64_t K) {
     constexpr int64_t CUS = 256;
     constexpr double BYTES_PER_KTILE = 9e6;
-    const int64_t tiles = ((M + QM - 1) / QM) * ((N + QN - 1) / QN), kt = K / TILE_K;
-    int best = 1;
-    double best_cost = (double)((tiles + CUS - 1) / CUS) * kt;
-    for (int s = 2; s <= 8 && kt / s >= 4; ++s) {
-        const double cost = (double)((tiles * s + CUS - 1) / CUS) * ((kt + s - 1) / s) +
-                            (double)s * M * N * 8 / BYTES_PER_KTILE;
-        if (cost < best_cost) {
-            best = s;
-            best_cost = cost;
+    const int64_t kt = K / TILE_K;
+    W4A16Plan best{4, 1};
+    double best_cost = 0;
+    for (int fn : {4, 2}) {
+        const int64_t qn = QW * fn * 16, tiles = ((M + QM - 1) / QM) * ((N + qn - 1) / qn);
+        const double ktile = fn == 4 ? 1.0 : 0.6;
+        for (int s = 1; s <= 8 && (s == 1 || kt / s >= 4); ++s) {
+            const double cost = (double)((tiles * s + CUS - 1) / CUS) * ((kt + s - 1) / s) * ktile +
+                                (s > 1 ? (double)s * M * N * 8 / BYTES_PER_KTILE : 0.0);
+            if (best_cost == 0 || cost < best_cost) {
+                best = W4A16Plan{fn, s};
+                best_cost = cost;
+            }
         }
     }
     return best;
+}
+
+int w4a16_tile_splits(int64_t M, int64_t N, int64_t K) { return w4a16_plan(M, N, K).splits; }
+
+hipError_t launch_gemm_w4a16(const LinParams& p, hipStream_t stream) {
+    return w4a16_plan(p.M, p.N, p.K).fn == 2 ? launch_fn<2>(p, stream) : launch_fn<4>(p, stream);
 }
 
 }  // namespace bql

@@ -235,13 +235,18 @@ struct ExactPlan {
 ExactPlan exact_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_exact(const LinParams& p, const ExactPlan& plan, hipStream_t stream);
 
-// Launch of the per-group W4A16 tile kernel (128 x 256 blocks, one 128 x 64
-// output tile per wave); defined in gemm_w4a16.hip.  w4a16_tile_fits tells
-// whether a shape is inside that kernel's offset range.
+// Launch of the per-group W4A16 tile kernel (128-row blocks of 256 or 128
+// columns, four waves side by side in N); defined in gemm_w4a16.hip.
+// w4a16_tile_fits tells whether a shape is inside that kernel's offset
+// range; w4a16_plan gives the block width (fn 16-channel strips per wave)
+// and K splits (fp32 partials in the workspace, then the split-K reduce).
+struct W4A16Plan {
+    int fn;
+    int splits;
+};
+W4A16Plan w4a16_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_w4a16(const LinParams& p, hipStream_t stream);
 bool w4a16_tile_fits(int64_t M, int64_t N, int64_t K);
-// K splits of the tile kernel at this shape (fp32 partials in the workspace,
-// then the split-K reduce); 1 when every CU already has a block.
 int w4a16_tile_splits(int64_t M, int64_t N, int64_t K);
 
 }  // namespace bql

@@ -54,11 +54,14 @@ def test_w4a16_group_workload(M, KN):
 # (77, 300, 130), a column block with waves wholly past N (272), one and
 # two k-tiles (the pipeline's shortest runs), odd k-tile counts (384), and
 # few blocks with a long K, whose k range is split over blocks (fp32
-# partial sums, then the split-K reduce): (200, 1040, 4096), (1024, 4096, 4096);
-# (8, 256, 65536): the small-M kernel with K split eight ways
+# partial sums, then the split-K reduce): (200, 1040, 4096); blocks of 128
+# columns at most of these shapes and 256 columns where 128 would take a
+# second round: (2000, 2064, 1024) unsplit, (520, 4208, 4096) in three K
+# splits; (8, 256, 65536): the small-M kernel with K split eight ways
 @pytest.mark.parametrize("M,N,K", [(77, 1040, 384), (3, 16, 128), (300, 272, 1280), (16, 2064, 4096),
                                    (1, 4096, 14336), (40, 512, 128), (130, 4096, 256), (17, 784, 640),
-                                   (200, 1040, 4096), (1024, 4096, 4096), (8, 256, 65536)])
+                                   (200, 1040, 4096), (1024, 4096, 4096), (8, 256, 65536),
+                                   (2000, 2064, 1024), (520, 4208, 4096)])
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16, torch.float32])
 def test_w4a16_group_ragged(M, N, K, out):
     g = wl.rng(94, M, N, K)
