@@ -50,9 +50,9 @@ __device__ __forceinline__ void load_a(const void* a, int64_t M, int64_t K, int6
 }
 
 // The lane's 32 codes of one k-tile as two 16-byte halves: codes as loaded,
-// or fp16 / bf16 cast as E4M3(x / sA) (quot_f32: the IEEE quotient).
-template <int SRC>
-__device__ __forceinline__ void codes_a(const ARaw<SRC>& r, double inv, u4 (&out)[2]) {
+// or fp16 / bf16 cast as E4M3(x / sA), enc2(a, b) giving the code pair.
+template <int SRC, class Enc>
+__device__ __forceinline__ void codes_a(const ARaw<SRC>& r, Enc enc2, u4 (&out)[2]) {
     if constexpr (SRC == 4) {
         out[0] = r.v[0];
         out[1] = r.v[1];
@@ -64,10 +64,8 @@ __device__ __forceinline__ void codes_a(const ARaw<SRC>& r, double inv, u4 (&out
             for (int j = 0; j < 4; ++j) {
                 const u4& v = r.v[2 * h + j / 2];
                 const uint32_t d0 = v[2 * (j & 1)], d1 = v[2 * (j & 1) + 1];
-                const uint32_t lo = e4m3_encode2(quot_f32(to_f32<SRC>(d0 & 0xFFFFu), inv),
-                                                 quot_f32(to_f32<SRC>(d0 >> 16), inv));
-                const uint32_t hi = e4m3_encode2(quot_f32(to_f32<SRC>(d1 & 0xFFFFu), inv),
-                                                 quot_f32(to_f32<SRC>(d1 >> 16), inv));
+                const uint32_t lo = enc2(to_f32<SRC>(d0 & 0xFFFFu), to_f32<SRC>(d0 >> 16));
+                const uint32_t hi = enc2(to_f32<SRC>(d1 & 0xFFFFu), to_f32<SRC>(d1 >> 16));
                 c[j] = lo | (hi << 16);
             }
             out[h] = u4{c[0], c[1], c[2], c[3]};
@@ -114,44 +112,58 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
     } else {
         sa = *scale;
     }
-    const double inv = 1.0 / (double)sa;
     v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    auto compute = [&](const ARaw<SRC> (&raw)[SK_BATCH], const u4 (&bv)[SK_BATCH][2]) {
+    // The main loop for a given encoder enc2(a, b) of the code pair of
+    // a / sA and b / sA.
+    auto main_loop = [&](auto enc2) __attribute__((always_inline)) {
+        auto compute = [&](const ARaw<SRC> (&raw)[SK_BATCH], const u4 (&bv)[SK_BATCH][2]) {
 #pragma unroll
-        for (int u = 0; u < SK_BATCH; ++u) {
-            u4 av[2];
-            codes_a<SRC>(raw[u], inv, av);
-            if constexpr (FAST) {
-                const v8i x = v8i{(int)av[0][0], (int)av[0][1], (int)av[0][2], (int)av[0][3],
-                                  (int)av[1][0], (int)av[1][1], (int)av[1][2], (int)av[1][3]};
-                const v8i y = v8i{(int)bv[u][0][0], (int)bv[u][0][1], (int)bv[u][0][2], (int)bv[u][0][3],
-                                  (int)bv[u][1][0], (int)bv[u][1][1], (int)bv[u][1][2], (int)bv[u][1][3]};
-                acc = mfma_fp8(x, y, acc);
-            } else {
-                // the lane's 32 codes of each operand, 8 at a time, widened
-                // losslessly to fp16: four 16x16x32 products per k-tile
+            for (int u = 0; u < SK_BATCH; ++u) {
+                u4 av[2];
+                codes_a<SRC>(raw[u], enc2, av);
+                if constexpr (FAST) {
+                    const v8i x = v8i{(int)av[0][0], (int)av[0][1], (int)av[0][2], (int)av[0][3],
+                                      (int)av[1][0], (int)av[1][1], (int)av[1][2], (int)av[1][3]};
+                    const v8i y = v8i{(int)bv[u][0][0], (int)bv[u][0][1], (int)bv[u][0][2], (int)bv[u][0][3],
+                                      (int)bv[u][1][0], (int)bv[u][1][1], (int)bv[u][1][2], (int)bv[u][1][3]};
+                    acc = mfma_fp8(x, y, acc);
+                } else {
+                    // the lane's 32 codes of each operand, 8 at a time, widened
+                    // losslessly to fp16: four 16x16x32 products per k-tile
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    acc = mfma_f16(e4m3x8_to_f16(av[h][0], av[h][1]),
-                                   e4m3x8_to_f16(bv[u][h][0], bv[u][h][1]), acc);
-                    acc = mfma_f16(e4m3x8_to_f16(av[h][2], av[h][3]),
-                                   e4m3x8_to_f16(bv[u][h][2], bv[u][h][3]), acc);
+                    for (int h = 0; h < 2; ++h) {
+                        acc = mfma_f16(e4m3x8_to_f16(av[h][0], av[h][1]),
+                                       e4m3x8_to_f16(bv[u][h][0], bv[u][h][1]), acc);
+                        acc = mfma_f16(e4m3x8_to_f16(av[h][2], av[h][3]),
+                                       e4m3x8_to_f16(bv[u][h][2], bv[u][h][3]), acc);
+                    }
                 }
             }
+        };
+        // Two batches per trip, the sets swapping roles without copies; a batch
+        // past K reads zero A and adds nothing.  The sched barriers keep each
+        // batch's loads ahead of the casts and multiplies before them (the
+        // scheduler would otherwise sink them behind waits).
+        for (int64_t kt = wave; kt < KT; kt += 2 * STEP) {
+            load_batch(kt + STEP, rb, wb);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ra, wa);
+            if (kt + STEP >= KT) break;  // this wave has no second batch
+            load_batch(kt + 2 * STEP, ra, wa);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(rb, wb);
         }
     };
-    // Two batches per trip, the sets swapping roles without copies; a batch
-    // past K reads zero A and adds nothing.  The sched barriers keep each
-    // batch's loads ahead of the casts and multiplies before them (the
-    // scheduler would otherwise sink them behind waits).
-    for (int64_t kt = wave; kt < KT; kt += 2 * STEP) {
-        load_batch(kt + STEP, rb, wb);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(ra, wa);
-        if (kt + STEP >= KT) break;  // this wave has no second batch
-        load_batch(kt + 2 * STEP, ra, wa);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(rb, wb);
+    // A dynamic scale (amax / 448 of this tensor, so every input is finite
+    // when the scale passes its range check) takes the reciprocal form and
+    // the encoder without NaN handling, as the standalone quantizer; a given
+    // scale the fp64-reciprocal IEEE quotient.
+    if (nparts > 0 && recip_div_ok(sa)) {
+        const float y = 1.0f / sa;
+        main_loop([&](float p0, float p1) { return e4m3_div2_finite(p0, p1, sa, y); });
+    } else {
+        const double inv = 1.0 / (double)sa;
+        main_loop([&](float p0, float p1) { return e4m3_encode2(quot_f32(p0, inv), quot_f32(p1, inv)); });
     }
     red[wave][lane] = acc;
     __syncthreads();
