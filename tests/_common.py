@@ -145,3 +145,52 @@ def exact_plan(M: int, N: int, K: int) -> tuple:
             if best_us is None or us < best_us:
                 best, best_us = (fn, s), us
     return best
+
+
+def gemv_splits(M: int, N: int, K: int, int4: bool = False) -> int:
+    """K splits of the small-M streaming kernel (M <= 16): among the split
+    counts that keep about 256 blocks at most (512 for K < 32 k-tiles) and 8
+    (4) k-tiles per split, the one the library's cost model picks: a block
+    streams its strip's weight bytes (2 KiB per k-tile, 1 KiB for int4) at
+    45 GB/s, and a split costs 3.6 us.  test_abi_host checks it against the
+    library's workspace sizes."""
+    KT = (K + 127) // 128
+    groups = (N // 16) * ((M + 15) // 16)
+    target, min_kt = (512, 4) if KT < 32 else (256, 8)
+    smax = 1
+    while groups * smax < target and smax * 2 <= 8 and KT // (smax * 2) >= min_kt:
+        smax *= 2
+    strip = KT * (1024 if int4 else 2048)
+    s, best = 1, strip / 45e3
+    c = 2
+    while c <= smax:
+        cost = 3.6 + strip / c / 45e3
+        if cost < best:
+            s, best = c, cost
+        c *= 2
+    per = (KT + s - 1) // s
+    return (KT + per - 1) // per
+
+
+def w4a16_plan(M: int, N: int, K: int) -> tuple:
+    """(fn, splits) of the per-group W4A16 tile kernel (M > 16): 128-row
+    blocks of 64 fn columns, the library's cost model in k-tile times of a
+    256-column block: rounds of 256 blocks times ceil(KT / s) k-tiles (a
+    128-column block's k-tile at 0.6), plus 8 bytes per output and split at
+    9 MB per k-tile time; at most 8 splits of 4+ k-tiles."""
+    kt = K // 128
+    best, best_cost = (4, 1), None
+    for fn in (4, 2):
+        qn = 64 * fn
+        tiles = ((M + 127) // 128) * ((N + qn - 1) // qn)
+        ktile = 1.0 if fn == 4 else 0.6
+        s = 1
+        while s <= 8 and (s == 1 or kt // s >= 4):
+            cost = ((tiles * s + 255) // 256) * ((kt + s - 1) // s) * ktile
+            if s > 1:
+                cost += s * M * N * 8 / 9e6
+            if best_cost is None or cost < best_cost:
+                best, best_cost = (fn, s), cost
+            s += 1
+    return best
+

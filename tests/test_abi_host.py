@@ -329,3 +329,44 @@ def test_exact_tile_plan_mirror(L):
                 checked += 1
     assert checked > 400
 
+
+def _split_ws(M, N, K, s):
+    KT = (K + 127) // 128
+    per = (KT + s - 1) // s
+    n = (KT + per - 1) // per
+    return (n * M * N * 4 + 255) // 256 * 256 if n > 1 else 0
+
+
+def test_small_m_split_plan_mirror(L):
+    """The test-side mirror of the small-M kernel's split plan gives the
+    partial buffers the library sizes its workspaces for (W8A16 and W4A8
+    run the small-M kernel at M <= 16)."""
+    from _common import gemv_splits
+    splits_seen = set()
+    for M in (1, 2, 4, 8, 16):
+        for N in (16, 256, 1024, 2048, 4096, 6144):
+            for K in (128, 1024, 4096, 8192, 16384, 34816, 65536):
+                s = gemv_splits(M, N, K)
+                assert L.bql_w8a16_linear_workspace_size(M, N, K) == _split_ws(M, N, K, s), (M, N, K, s)
+                s4 = gemv_splits(M, N, K, int4=True)
+                aq = ((M + 15) // 16) * ((K + 127) // 128) * 2048  # the packed-A region
+                got = L.bql_w4a8_linear_workspace_size(M, N, K) - (aq + 255) // 256 * 256
+                assert got == _split_ws(M, N, K, s4), (M, N, K, s4)
+                splits_seen |= {s, s4}
+    assert {1, 2, 4, 8} <= splits_seen
+
+
+def test_w4a16_tile_plan_mirror(L):
+    """The test-side mirror of the per-group W4A16 tile kernel's plan gives
+    the split count the library sizes its workspace for, and both block
+    widths occur."""
+    from _common import w4a16_plan
+    widths = set()
+    for M in (17, 100, 256, 512, 1000, 1024, 2048, 4096):
+        for N in (272, 1040, 2064, 4096, 5120, 6656, 8192):
+            for K in (128, 1024, 4096, 5120, 8192, 14336):
+                fn, s = w4a16_plan(M, N, K)
+                assert L.bql_w4a16_linear_workspace_size(M, N, K) == _split_ws(M, N, K, s), (M, N, K, fn, s)
+                widths.add(fn)
+    assert widths == {2, 4}
+
