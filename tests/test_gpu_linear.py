@@ -186,7 +186,8 @@ def test_fp8_ragged(M, N, K):
     _fp8_case(8, N * 1000 + K, M, N, K, "bf16", True, "entries", torch.bfloat16, rows_count=400)
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 40])
+# W8A16 streams the weight once per 16-row batch at every M
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 40, 129])
 @pytest.mark.parametrize("N,K", [(48, 144), (272, 400)])
 def test_w8a16_ragged(M, N, K):
     g = wl.rng(9, N, K)
@@ -200,7 +201,9 @@ def test_w8a16_ragged(M, N, K):
                  f"W8A16 M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 17, 130])
+# M = 16 / 17: the small-M kernel / the 128 x 128 tile kernel; 128 / 129 /
+# 257: one full row tile, one row past it, two tiles and one row
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 128, 129, 130, 257])
 @pytest.mark.parametrize("N,K", [(48, 144), (272, 400)])
 def test_w4a8_ragged(M, N, K):
     g = wl.rng(10, N, K)
