@@ -109,7 +109,7 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
     auto body = [&](auto enc2) {
         for (int64_t i = (int64_t)blockIdx.x * QT + threadIdx.x; i < nvec;
              i += (int64_t)gridDim.x * QT) {
-            u4 v = __builtin_nontemporal_load(&xv[i]);
+            u4 v = xv[i];  // plain load: x was just read by the amax pass
             uint32_t c[4];  // code pairs
 #pragma unroll
             for (int j = 0; j < 4; ++j) c[j] = enc2(to_f32<DT>(v[j] & 0xFFFFu), to_f32<DT>(v[j] >> 16));
@@ -141,7 +141,10 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
 // The 32 inputs of lane (r, g) for packed tile t: row 16 mt + r, k = 128 kt
 // + 32 g .. +31, as two halves of two 16-byte loads.  Rows past M and k
 // past K (K is a multiple of 16) read as zero; every load is issued (from a
-// valid address when out of range) so that none sits in a branch.
+// valid address when out of range) so that none sits in a branch.  Plain
+// loads, not nontemporal ones: the amax pass has just read x, and plain
+// loads find more of it still cached (the Llama-3-8B fp8 step at M = 1024
+// is 0.7 % faster).
 struct TileIn {
     u4 v[2][2];
 };
@@ -154,7 +157,7 @@ __device__ __forceinline__ void load_tile_in(const uint16_t* __restrict__ x, int
     for (int h = 0; h < 2; ++h) {
         const bool ok = m < M && k + 16 * h < K;
         const u4* src = (const u4*)(ok ? x + m * K + k + 16 * h : x);
-        const u4 v0 = __builtin_nontemporal_load(src), v1 = __builtin_nontemporal_load(src + 1);
+        const u4 v0 = src[0], v1 = src[1];
         in.v[h][0] = ok ? v0 : u4{0u, 0u, 0u, 0u};
         in.v[h][1] = ok ? v1 : u4{0u, 0u, 0u, 0u};
     }
