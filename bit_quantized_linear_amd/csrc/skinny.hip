@@ -11,9 +11,11 @@
 // next batch is requested before the current one is cast and multiplied,
 // and the first batch before the activation scale is read.  A lane's 32 operand bytes of a
 // 16 x 128 tile are 32 consecutive k of one row (row = lane % 16, k =
-// 32 * (lane / 16) + 0..31, the packed layout's lane map), so A is read
-// where it is, row-major: E4M3 codes as they are, fp16 / bf16 cast to codes
-// in registers (no packed copy of A is written).  The W tile comes from the
+// 32 * (lane / 16) + 0..31, the packed layout's lane map).  A is read where
+// it is, row-major, by loads that each cover whole lines of a few rows, and
+// regrouped into that lane map through a small LDS area per wave: E4M3
+// codes as they are, fp16 / bf16 then cast to codes in registers (no packed
+// copy of A is written).  The W tile comes from the
 // single weight strip, which stays in L2.  The 8 partial 16x16 accumulators
 // are summed through LDS in a fixed order and wave 0 applies the epilogue
 // to the N real columns.
@@ -25,29 +27,57 @@ constexpr int SK_WAVES = 8;
 constexpr int SK_BATCH = 2;  // k-tiles per register set (two sets alternate)
 constexpr int SRC_CODES = 4;
 
-// Raw loads of the lane's 32 values of A for one k-tile (row m, k0..k0+31):
-// two 16-byte chunks of E4M3 codes, or four of fp16 / bf16.  Rows past M and
-// chunks past K (a multiple of 16) read as zero.  Plain loads: with a dynamic
-// scale the amax pass has just read A, and plain loads find more of it
-// cached than nontemporal ones (the router call 8 % faster end to end).
+// A lane's share of one 16 x 128 tile of A: two 16-byte chunks of E4M3
+// codes, or four of fp16 / bf16.
 template <int SRC>
 struct ARaw {
     static constexpr int N = SRC == 4 ? 2 : 4;
     u4 v[N];
 };
 
+// Row-contiguous loads of one 16 x 128 tile of A (columns k0 ..): codes as
+// two loads where lane L takes row 8q + L/8, chunk L%8; fp16 / bf16 as four
+// loads where lane L takes row 4q + L/16, chunk L%16.  Each instruction
+// reads whole 128-byte lines (the operand layout's own lane map would touch
+// 16 rows in 16-byte pieces per instruction: the dynamic router call 7 %
+// slower).  Rows past M and chunks past K (a multiple of 16) read as zero.
+// Plain loads: with a dynamic scale the amax pass has just read A, and
+// plain loads find more of it cached than nontemporal ones (8 %).
 template <int SRC>
-__device__ __forceinline__ void load_a(const void* a, int64_t M, int64_t K, int64_t m, int64_t k0,
-                                       ARaw<SRC>& r) {
-    constexpr int STEP = SRC == 4 ? 16 : 8;  // elements per 16-byte chunk
-    constexpr int ES = SRC == 4 ? 1 : 2;     // bytes per element
+__device__ __forceinline__ void load_a_rows(const void* a, int64_t M, int64_t K, int64_t mt, int64_t k0,
+                                            int lane, ARaw<SRC>& r) {
+    constexpr int ES = SRC == 4 ? 1 : 2;
+    constexpr int LPR = SRC == 4 ? 8 : 16;   // lanes per row
+    constexpr int RPI = 64 / LPR;            // rows per instruction
+    constexpr int STEP = 16 / ES;            // elements per chunk
     const uint8_t* base = (const uint8_t*)a;
 #pragma unroll
     for (int q = 0; q < ARaw<SRC>::N; ++q) {
-        const bool ok = m < M && k0 + STEP * q < K;
-        const u4 v = *(const u4*)(ok ? base + (m * K + k0 + STEP * q) * ES : base);
+        const int64_t m = mt * 16 + RPI * q + lane / LPR;
+        const int64_t k = k0 + STEP * (lane % LPR);
+        const bool ok = m < M && k < K;
+        const u4 v = *(const u4*)(ok ? base + (m * K + k) * ES : base);
         r.v[q] = ok ? v : u4{0u, 0u, 0u, 0u};
     }
+}
+
+// Regroups a row-contiguous tile into the operand layout (lane (r, g) holds
+// row r, k 32 g .. 32 g + 31) through the wave's own 16 LDS rows (one
+// 16-byte pad per row).  LDS instructions of one wave execute in order, so
+// each wait only orders the compiler's code and hands the read data over;
+// the wave's next tile overwrites the rows only after these reads.
+template <int SRC>
+__device__ __forceinline__ void to_operand(ARaw<SRC>& r, u4* lds, int lane) {
+    constexpr int LPR = SRC == 4 ? 8 : 16;
+    constexpr int RPI = 64 / LPR;
+    constexpr int RS = LPR + 1;  // u4 per LDS row (one pad)
+    constexpr int NQ = ARaw<SRC>::N;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) lds[(RPI * q + lane / LPR) * RS + lane % LPR] = r.v[q];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) r.v[j] = lds[(lane & 15) * RS + NQ * (lane >> 4) + j];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // The lane's 32 codes of one k-tile as two 16-byte halves: codes as loaded,
@@ -81,10 +111,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
     float* __restrict__ scale_out, Epilogue ep) {
     __shared__ v4f red[SK_WAVES][64];
     __shared__ uint32_t sh[16];
+    __shared__ u4 lds_a[SK_WAVES][16 * 17];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t mt = blockIdx.x;
-    const int64_t m = mt * TILE_N + (lane & 15);
-    const int64_t kl = 32 * (lane >> 4);
     const uint8_t* wt = w + lane * 16;
     ARaw<SRC> ra[SK_BATCH], rb[SK_BATCH];
     u4 wa[SK_BATCH][2], wb[SK_BATCH][2];
@@ -93,7 +122,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
         for (int u = 0; u < SK_BATCH; ++u) {
             const int64_t kt = kt0 + u * SK_WAVES;
             const int64_t kv = kt < KT ? kt : 0;  // past K: a valid tile, multiplied by zero A
-            load_a<SRC>(a, M, K, m, kt * TILE_K + kl, raw[u]);  // k past K reads as zero
+            load_a_rows<SRC>(a, M, K, mt, kt * TILE_K, lane, raw[u]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) bv[u][h] = *(const u4*)(wt + kv * FP8_TILE_BYTES + h * 1024);
         }
@@ -121,7 +150,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_linear_kernel(
 #pragma unroll
             for (int u = 0; u < SK_BATCH; ++u) {
                 u4 av[2];
-                codes_a<SRC>(raw[u], enc2, av);
+                ARaw<SRC> t = raw[u];
+                to_operand<SRC>(t, lds_a[wave], lane);
+                codes_a<SRC>(t, enc2, av);
                 if constexpr (FAST) {
                     const v8i x = v8i{(int)av[0][0], (int)av[0][1], (int)av[0][2], (int)av[0][3],
                                       (int)av[1][0], (int)av[1][1], (int)av[1][2], (int)av[1][3]};
