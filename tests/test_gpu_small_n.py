@@ -29,10 +29,12 @@ def _weight(N, K, dtype, seed):
 
 
 # (M, N, K): router shapes (8 experts on Llama-3-8B / Mixtral-like hidden
-# sizes), every M regime, ragged M, odd N, minimal K
+# sizes), every M regime, ragged M, odd N, minimal K; ragged M with a
+# partial last k-tile (A is loaded in whole rows of a tile and regrouped, so
+# rows past M and chunks past K must read as zero in that mapping too)
 CASES = [(1, 8, 4096), (16, 8, 4096), (128, 8, 4096), (1024, 8, 4096), (4096, 8, 4096),
          (1000, 8, 5120), (37, 1, 4096), (300, 3, 1024), (64, 15, 8192), (5, 8, 16),
-         (33, 12, 48), (2048, 2, 14336)]
+         (33, 12, 48), (2048, 2, 14336), (19, 8, 400), (260, 5, 4112)]
 
 
 @pytest.mark.parametrize("M,N,K", CASES)
@@ -61,9 +63,9 @@ def test_small_n_dynamic(M, N, K, per_channel):
     assert_fast_bound(host_f64(yf)[rows], ref, abs_sum, f"M={M} N={N} fast accumulation")
 
 
-@pytest.mark.parametrize("M", [1, 256])
-def test_small_n_prequantized_static_and_fp8_out(M):
-    N, K = 8, 4096
+@pytest.mark.parametrize("M,K", [(1, 4096), (256, 4096), (37, 400)])
+def test_small_n_prequantized_static_and_fp8_out(M, K):
+    N = 8
     wb, wf = _weight(N, K, "f16", 3)
     pw = bql.prepack_weight(dev16(wb, "f16"), "fp8_tensor")
     codes, sw = oracle.quant_per_tensor(wf)
