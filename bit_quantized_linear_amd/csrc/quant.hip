@@ -138,53 +138,50 @@ __global__ __launch_bounds__(QT) void cast_e4m3_kernel(const uint16_t* __restric
 // row l % 16 and k = 32*(l/16) + 16*h + j.  Columns k >= K up to the tile
 // edge and rows past M in the last strip hold zero codes.
 
-// The 32 inputs of lane (r, g) for packed tile t: row 16 mt + r, k = 128 kt
-// + 32 g .. +31, as two halves of two 16-byte loads.  Rows past M and k
+// One wave's inputs of packed tile t (16 rows x 128 k).  Rows past M and k
 // past K (K is a multiple of 16) read as zero; every load is issued (from a
 // valid address when out of range) so that none sits in a branch.  Plain
 // loads, not nontemporal ones: the amax pass has just read x, and plain
 // loads find more of it still cached (the Llama-3-8B fp8 step at M = 1024
-// is 0.7 % faster).
+// is 0.7 % faster).  Loads cover whole lines of 4 rows each, and each
+// lane stores its codes where the operand layout puts them (the layout's
+// own lane map as the load map touches 16 rows in 16-byte pieces per
+// instruction: the step 0.6 % slower).
 struct TileIn {
-    u4 v[2][2];
+    u4 v[4];
 };
 
+// Row-contiguous loads: load q of lane L takes row 4q + L/16 of the tile,
+// inputs k = 128 kt + 8 (L%16) .. +7 (whole 128-byte lines per instruction).
 __device__ __forceinline__ void load_tile_in(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                              int64_t KT, int64_t t, int r, int g, TileIn& in) {
+    const int lane = r + 16 * g;
     const int64_t mt = t / KT, kt = t % KT;
-    const int64_t m = mt * 16 + r, k = kt * 128 + 32 * g;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const bool ok = m < M && k + 16 * h < K;
-        const u4* src = (const u4*)(ok ? x + m * K + k + 16 * h : x);
-        const u4 v0 = src[0], v1 = src[1];
-        in.v[h][0] = ok ? v0 : u4{0u, 0u, 0u, 0u};
-        in.v[h][1] = ok ? v1 : u4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < 4; ++q) {
+        const int64_t m = mt * 16 + 4 * q + (lane >> 4), k = kt * 128 + 8 * (lane & 15);
+        const bool ok = m < M && k < K;
+        const u4 v = *(const u4*)(ok ? x + m * K + k : x);
+        in.v[q] = ok ? v : u4{0u, 0u, 0u, 0u};
     }
 }
 
-// Codes of one tile's inputs (enc2(a, b): the code pair of a / s and b / s),
-// stored at tile t + 16 l (k .. k+15) and tile t + 1024 + 16 l (k+16 ..
-// k+31).  Zero inputs give zero codes.
+// The 8 codes of each load go to their place in the operand tile: row rr,
+// k = 8 c .. lies in lane rr + 16 (c / 4), half (c % 4) / 2, bytes 8 (c % 2).
 template <int DT, class Enc>
 __device__ __forceinline__ void store_tile_codes(const TileIn& in, uint8_t* __restrict__ xq,
                                                  int64_t t, int lane, Enc enc2) {
-    u4 out[2];
+    const int c = lane & 15;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t c[8];  // code pairs
+    for (int q = 0; q < 4; ++q) {
+        const int rr = 4 * q + (lane >> 4);
+        const u4& v = in.v[q];
+        uint32_t p[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u4& v0 = in.v[h][0];
-            const u4& v1 = in.v[h][1];
-            c[j] = enc2(to_f32<DT>(v0[j] & 0xFFFFu), to_f32<DT>(v0[j] >> 16));
-            c[4 + j] = enc2(to_f32<DT>(v1[j] & 0xFFFFu), to_f32<DT>(v1[j] >> 16));
-        }
-        out[h] = u4{c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+        for (int j = 0; j < 4; ++j) p[j] = enc2(to_f32<DT>(v[j] & 0xFFFFu), to_f32<DT>(v[j] >> 16));
+        uint8_t* dst = xq + t * 2048 + ((c & 3) >> 1) * 1024 + (rr + 16 * (c >> 2)) * 16 + 8 * (c & 1);
+        *(u2*)dst = u2{p[0] | (p[1] << 16), p[2] | (p[3] << 16)};
     }
-    uint8_t* tile = xq + t * 2048 + lane * 16;
-    *(u4*)tile = out[0];
-    *(u4*)(tile + 1024) = out[1];
 }
 
 // The tile loop of the packed casts, for a given encoder enc2(a, b) of the
